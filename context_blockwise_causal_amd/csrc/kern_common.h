@@ -1,0 +1,100 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// v_mfma_f32_32x32x16_bf16: A is 32(M) x 16(K), B is 16(K) x 32(N), C/D 32 x 32 fp32.
+// Lane l supplies A row (l % 32) and B column (l % 32), 8 K-values each (the K index of
+// element e in lane half h = l / 32 is the same for A and B, so the contraction is correct
+// for any consistent K order).  The accumulator register r = 4*j + i (j, i in 0..3) of lane l
+// holds C[8*j + 4*(l/32) + i][l % 32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row order used when an MFMA *output* row index must become a K index of a following
+// MFMA.  Output row rho = 8j + 4h + i lives in lane half h, register 4j + i.  Feeding A row
+// rho with source row perm32(rho) makes lane half h hold source rows 16*c + 8*h + e
+// (e = 0..7) in registers 8*c + e, c = 0, 1: exactly the 8-consecutive K rows that a
+// 32x32x16 operand wants from that lane half.
+__device__ __forceinline__ int perm32(int rho) {
+  const int j = rho >> 3, h = (rho >> 2) & 1, i = rho & 3;
+  return ((j >> 1) << 4) | (h << 3) | ((j & 1) << 2) | i;
+}
+
+// Source row (0..31) held in accumulator register r of lane half h after perm32.
+__device__ __forceinline__ int perm_reg_row(int r, int h) {
+  const int j = r >> 2, i = r & 3;
+  return ((j >> 1) << 4) | (h << 3) | ((j & 1) << 2) | i;
+}
+
+// Plain (unpermuted) output row of accumulator register r in lane half h.
+__device__ __forceinline__ int out_row(int r, int h) { return ((r >> 2) << 3) | (h << 2) | (r & 3); }
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+  return r;
+}
+
+// Gathers 8 bf16 values at stride `pitch` elements (one column of 8 consecutive rows).
+__device__ __forceinline__ bf16x8 gather8(const u16* p, int pitch) {
+  u32x4 w;
+  w[0] = (unsigned)p[0] | ((unsigned)p[pitch] << 16);
+  w[1] = (unsigned)p[2 * pitch] | ((unsigned)p[3 * pitch] << 16);
+  w[2] = (unsigned)p[4 * pitch] | ((unsigned)p[5 * pitch] << 16);
+  w[3] = (unsigned)p[6 * pitch] | ((unsigned)p[7 * pitch] << 16);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+struct TileRef {
+  int b, hq, g, range;
+  int64_t row0;  // first outer row of the tile (in the operand's rows)
+  int nrows;     // rows of the tile inside its range (<= tile rows)
+};
+
+// Maps the hardware workgroup index to (batch, head, tile).  Workgroup i is dispatched to
+// XCD i % 8; each XCD is given one contiguous run of the logical order so that the query
+// heads sharing a key/value head (adjacent in the logical order) meet in the same L2.  The
+// logical order is batch, head (kv-head major), then tiles heaviest first.
+__device__ __forceinline__ TileRef map_tile(const KParams& p, int64_t tile_rows) {
+  const int64_t nblk = (int64_t)gridDim.x;
+  const int64_t bid = (int64_t)blockIdx.x;
+  const int64_t x = bid & 7, k = bid >> 3;
+  const int64_t q = nblk >> 3, rem = nblk & 7;
+  const int64_t logical = x * q + (x < rem ? x : rem) + k;
+  const int64_t head = logical / p.tiles_per_head;
+  int64_t t = logical - head * p.tiles_per_head;
+  TileRef r;
+  r.b = (int)(head / p.Hq);
+  r.hq = (int)(head - (int64_t)r.b * p.Hq);
+  r.g = r.hq / p.n_rep;
+  int ri = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (i < p.nranges && t >= p.ranges[i].tile0) ri = i;
+  const KRange& R = p.ranges[ri];
+  t -= R.tile0;
+  if (R.reverse) t = R.ntiles - 1 - t;
+  r.range = ri;
+  r.row0 = R.row0 + t * tile_rows;
+  const int64_t left = R.len - t * tile_rows;
+  r.nrows = (int)(left < tile_rows ? left : tile_rows);
+  return r;
+}
+
+}  // namespace ra

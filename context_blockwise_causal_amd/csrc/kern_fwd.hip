@@ -1,0 +1,249 @@
+// Chunk forward on bf16 MFMA (gfx950): folds K/V blocks into the running online-softmax
+// state (U, m, l) of a tile of query rows.
+//
+// Method: lecture note "上下文并行", section "朴素 Ring Attention": the safe softmax (row
+// max subtracted) and the FlashAttention-2-style update of the output block per K/V block,
+// which lets a rank fold the ring's chunks one at a time in any order.  Numerics per
+// "Feat: Context Parallel" section 数值精度: statistics and accumulation stay fp32, the
+// probabilities are rounded to bf16 only as the MFMA operand.
+//
+// Layout of the work (one workgroup = 4 wavefronts = 128 query rows of one (batch, head)):
+//  * Each wavefront owns 32 query rows.  Scores are computed transposed, S^T = K Q^T, on
+//    v_mfma_f32_32x32x16_bf16 so that a lane owns one query (column) and holds 16 keys per
+//    32-key block in registers: the row max and row sum are in-register reductions plus a
+//    single exchange with the other lane half.
+//  * The output is accumulated transposed too, O^T += V^T P^T: the probabilities stay in the
+//    registers they were computed in (the K rows were fed in perm32 order for that) and the
+//    per-query rescale factor is one scalar per lane.
+//  * K/V tiles of 64 keys are staged in LDS (double buffered, 16-byte coalesced global loads,
+//    prefetched into registers one tile ahead), shared by the 4 wavefronts.
+//  * exp2 with the softmax scale folded into log2(e): p = 2^(s*scale*log2e - m2).
+#include "kern_common.h"
+
+namespace ra {
+namespace {
+
+constexpr int kNT = 256;  // threads per workgroup
+constexpr int kBM = 128;  // query rows per workgroup
+constexpr int kBN = 64;   // keys per K/V tile
+
+template <int D>
+struct FwdCfg {
+  static constexpr int P = D + 8;                      // LDS row pitch (elements), 16B multiple
+  static constexpr int KK = D / 16;                    // k-steps of S^T over the head dim
+  static constexpr int DB = D / 32;                    // 32-row blocks of O^T
+  static constexpr int VROW = D / 8;                   // 16-byte vectors per row
+  static constexpr int LOADS = kBN * VROW / kNT;       // vectors per thread per tile, per tensor
+  static constexpr int TILE = kBN * P;                 // elements of one K (or V) LDS tile
+  static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(const u16* __restrict__ K, const u16* __restrict__ V,
+                                        int64_t key0, int64_t kv_len, u32x4* kr, u32x4* vr) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int u = threadIdx.x + kNT * i;
+    const int row = u / C::VROW, col = (u % C::VROW) * 8;
+    const int64_t key = key0 + row;
+    if (key < kv_len) {
+      kr[i] = *reinterpret_cast<const u32x4*>(K + key * D + col);
+      vr[i] = *reinterpret_cast<const u32x4*>(V + key * D + col);
+    } else {
+      kr[i] = u32x4{0u, 0u, 0u, 0u};
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv(u16* __restrict__ buf, const u32x4* kr, const u32x4* vr) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int u = threadIdx.x + kNT * i;
+    const int row = u / C::VROW, col = (u % C::VROW) * 8;
+    *reinterpret_cast<u32x4*>(buf + row * C::P + col) = kr[i];
+    *reinterpret_cast<u32x4*>(buf + C::TILE + row * C::P + col) = vr[i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p) {
+  using C = FwdCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) u16 lds[];
+
+  const TileRef tr = map_tile(p, kBM);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int qi = 32 * w + lq;  // this lane's query row within the tile
+  const bool qvalid = qi < tr.nrows;
+  const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
+  const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
+  const u16* __restrict__ Q = reinterpret_cast<const u16*>(p.q);
+  const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k);
+  const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v);
+
+  // B operand of S^T = K Q^T: lane holds Q[query][kk*16 + 8*hh .. +8].
+  bf16x8 qreg[C::KK];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) {
+    if (qvalid)
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + kk * 16 + 8 * hh);
+    else
+      qreg[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // Running state of this lane's query, O^T accumulator layout: oacc[db][4j+i] holds
+  // U[query][32*db + 8*j + 4*hh + i].
+  f32x16 oacc[C::DB];
+  float m2 = -__builtin_inff(), lsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  if (qvalid) {
+    m2 = p.m[qrow] * kLog2e;
+    lsum = p.l[qrow];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][4 * j + i] = u[i];
+      }
+  }
+
+  const KRange& R = p.ranges[tr.range];
+  for (int pi = 0; pi < R.npairs; ++pi) {
+    const KPair pr = p.pairs[R.pair[pi]];
+    const bool diag = pr.mask == RA_MASK_DIAG;
+    const int64_t qloc0 = tr.row0 - pr.q_row0;  // pair-local index of the tile's first query
+    const int64_t iq = qloc0 + qi;              // pair-local index of this lane's query
+    int64_t key_end = pr.kv_len;
+    if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
+    const int nkt = (int)((key_end + kBN - 1) / kBN);
+    const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
+    const u16* Vp = Vg + (kvhead + pr.kv_row0) * D;
+    const int64_t wq_first = qloc0 + 32 * w;  // pair-local index of the wavefront's first query
+    const bool wave_has_rows = 32 * w < tr.nrows;
+
+    u32x4 kr[C::LOADS], vr[C::LOADS];
+    load_kv<D>(Kp, Vp, 0, pr.kv_len, kr, vr);
+    store_kv<D>(lds, kr, vr);
+    __syncthreads();
+
+    for (int kt = 0; kt < nkt; ++kt) {
+      const u16* buf = lds + (kt & 1) * 2 * C::TILE;
+      const int64_t kbase = (int64_t)kt * kBN;
+      if (kt + 1 < nkt) load_kv<D>(Kp, Vp, kbase + kBN, pr.kv_len, kr, vr);
+
+      // Skip the math when the whole tile lies in the future of every query of this wave.
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
+      if (active) {
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+          const u16* krow = buf + (kb * 32 + perm32(lq)) * C::P + 8 * hh;
+#pragma unroll
+          for (int kk = 0; kk < C::KK; ++kk)
+            s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qreg[kk], s[kb]);
+        }
+        const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float v = s[kb][r] * p.scale_log2;
+            if (edge) {
+              const int64_t kj = kbase + kb * 32 + perm_reg_row(r, hh);
+              if (kj >= pr.kv_len || (diag && kj > iq)) v = -__builtin_inff();
+            }
+            s[kb][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m2, mx);
+        const float base = mnew == -__builtin_inff() ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m2 - base);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[kb][r] - base);
+            s[kb][r] = e;
+            rs += e;
+          }
+        rs += __shfl_xor(rs, 32);
+        lsum = lsum * alpha + rs;
+        m2 = mnew;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+
+        // B operand P^T for key step c (16 keys): registers 8*(c&1) .. +8 of block c>>1.
+        bf16x8 pb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bf16x8 t;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = (__bf16)s[c >> 1][8 * (c & 1) + e];
+          pb[c] = t;
+        }
+        const u16* vt = buf + C::TILE;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7.
+            const bf16x8 a = gather8(vt + (16 * c + 8 * hh) * C::P + 32 * db + lq, C::P);
+            oacc[db] = mfma32(a, pb[c], oacc[db]);
+          }
+      }
+      if (kt + 1 < nkt) store_kv<D>(lds + ((kt + 1) & 1) * 2 * C::TILE, kr, vr);
+      __syncthreads();
+    }
+  }
+
+  if (qvalid) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = oacc[db][4 * j + i];
+        *reinterpret_cast<f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh) = u;
+      }
+    if (hh == 0) {
+      p.m[qrow] = m2 * kLn2;
+      p.l[qrow] = lsum;
+    }
+  }
+}
+
+template <int D>
+int launch_fwd(const KParams& kp, void* stream) {
+  static bool attr_done = false;
+  const size_t lds = FwdCfg<D>::LDS_BYTES;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_fwd_bf16_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    attr_done = true;
+  }
+  const int64_t nblk = (int64_t)kp.B * kp.Hq * kp.tiles_per_head;
+  if (nblk == 0) return 0;
+  hipLaunchKernelGGL(chunk_fwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), lds,
+                     (hipStream_t)stream, kp);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_chunk_fwd_bf16(const KParams& kp, void* stream) {
+  return kp.D == 128 ? launch_fwd<128>(kp, stream) : launch_fwd<64>(kp, stream);
+}
+
+}  // namespace ra

@@ -1,0 +1,282 @@
+// Memory-bound kernels of the rank view: layout permutation, state init / merge / finalize,
+// the backward's delta pre-pass, casts, fills and the staging copy.  All are HBM-bound
+// streaming kernels: 16-byte vector loads/stores, one pass, no reuse.
+#include "kern_common.h"
+
+namespace ra {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- layout permutation ---------------------------------------------------------------------
+// Row lr of the gathered tensor (ranks [rank_begin, rank_begin + rank_count), owner after
+// owner) maps to a global row of the full tensor: contiguous slice r is rows
+// [r*chunk, (r+1)*chunk); a zigzag slice is chunk r then chunk 2cp-1-r of 2cp equal chunks.
+__global__ __launch_bounds__(kThreads) void layout_kernel(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ dst, int zigzag,
+                                                          unsigned cp, unsigned rank_begin,
+                                                          unsigned chunk, unsigned crow,
+                                                          unsigned rows_out, unsigned vec_shift,
+                                                          unsigned long long S, int gather) {
+  const unsigned idx = blockIdx.x * kThreads + threadIdx.x;
+  const unsigned vecs = rows_out << vec_shift;
+  if (idx >= vecs) return;
+  const unsigned lr = idx >> vec_shift;
+  const unsigned vec = idx & ((1u << vec_shift) - 1);
+  const unsigned rank = rank_begin + lr / chunk;
+  const unsigned w = lr % chunk;
+  unsigned long long grow;
+  if (zigzag) {
+    const unsigned which = w / crow, off = w % crow;
+    const unsigned c = which == 0 ? rank : 2 * cp - 1 - rank;
+    grow = (unsigned long long)c * crow + off;
+  } else {
+    grow = (unsigned long long)rank * chunk + w;
+  }
+  const unsigned long long head = blockIdx.y;
+  const unsigned long long full_i = ((head * S + grow) << vec_shift) + vec;
+  const unsigned long long part_i = ((head * rows_out + lr) << vec_shift) + vec;
+  if (gather) dst[part_i] = src[full_i];
+  else dst[full_i] = src[part_i];
+}
+
+// ---- online-softmax state ---------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void state_init_kernel(f32x4* __restrict__ U, float* __restrict__ m,
+                                                              float* __restrict__ l, long long nrows,
+                                                              int vec_per_row) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i < nrows * vec_per_row) U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (i < nrows) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.f;
+  }
+}
+
+// exp(a - b) with an empty left side (a = -inf) giving 0 and no NaN when b = -inf too.
+__device__ __forceinline__ float rescale(float a, float b) {
+  if (a == -__builtin_inff()) return 0.f;
+  return __expf(a - b);
+}
+
+// One thread per 4 floats of a row; all threads of a row recompute the row's two factors.
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(const f32x4* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             f32x4* __restrict__ U, float* __restrict__ m,
+                                                             float* __restrict__ l, long long nrows,
+                                                             int vec_shift) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (nrows << vec_shift)) return;
+  const long long row = i >> vec_shift;
+  const float mo = m[row], lp = lse_part[row];
+  const float mn = fmaxf(mo, lp);
+  const float a = rescale(mo, mn), b = rescale(lp, mn);
+  const f32x4 u = U[i], o = o_part[i];
+  U[i] = a * u + b * o;
+  // the row's scalars are updated only after every vector of the row has read them: the
+  // scalar writer is the row's last vector, and the row's vectors live in one wavefront for
+  // head_dim <= 256, which executes the reads above before this write.
+  if ((i & ((1ll << vec_shift) - 1)) == ((1ll << vec_shift) - 1)) {
+    m[row] = mn;
+    l[row] = a * l[row] + b;
+  }
+}
+
+__device__ __forceinline__ u16 f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(u16, (__bf16)f);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const f32x4* __restrict__ U,
+                                                            const float* __restrict__ m,
+                                                            const float* __restrict__ l,
+                                                            void* __restrict__ o,
+                                                            float* __restrict__ lse, long long nrows,
+                                                            int vec_shift) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (nrows << vec_shift)) return;
+  const long long row = i >> vec_shift;
+  const float lr = l[row];
+  const float inv = lr > 0.f ? 1.0f / lr : 0.f;
+  const f32x4 v = U[i] * inv;
+  if (BF16) {
+    const unsigned lo = (unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+    const unsigned hi = (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+    reinterpret_cast<uint2*>(o)[i] = make_uint2(lo, hi);
+  } else {
+    reinterpret_cast<f32x4*>(o)[i] = v;
+  }
+  if ((i & ((1ll << vec_shift) - 1)) == 0)
+    lse[row] = lr > 0.f ? m[row] + logf(lr) : -__builtin_inff();
+}
+
+// delta = rowsum(dO * O): 16 lanes per row, each summing D/16 products, then a 16-lane
+// butterfly.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void preprocess_kernel(const void* __restrict__ o,
+                                                              const void* __restrict__ dO,
+                                                              float* __restrict__ delta,
+                                                              long long nrows, int D) {
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long row = t >> 4;
+  const int sub = (int)(t & 15);
+  float acc = 0.f;
+  if (row < nrows) {
+    const int per = D / 16;  // 4 or 8 elements
+    const long long base = row * D + sub * per;
+    if (BF16) {
+      const u16* a = reinterpret_cast<const u16*>(o) + base;
+      const u16* b = reinterpret_cast<const u16*>(dO) + base;
+      for (int e = 0; e < per; ++e) {
+        const float x = __builtin_bit_cast(float, (unsigned)a[e] << 16);
+        const float y = __builtin_bit_cast(float, (unsigned)b[e] << 16);
+        acc = fmaf(x, y, acc);
+      }
+    } else {
+      const float* a = reinterpret_cast<const float*>(o) + base;
+      const float* b = reinterpret_cast<const float*>(dO) + base;
+      for (int e = 0; e < per; ++e) acc = fmaf(a[e], b[e], acc);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (row < nrows && sub == 0) delta[row] = acc;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const f32x4* __restrict__ src,
+                                                        void* __restrict__ dst, long long nvec) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nvec) return;
+  const f32x4 v = src[i];
+  if (BF16) {
+    const unsigned lo = (unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+    const unsigned hi = (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2(lo, hi);
+  } else {
+    reinterpret_cast<f32x4*>(dst)[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(f32x4* __restrict__ dst, long long nvec) {
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+    dst[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// blocks x (block_bytes / 16) vectors; grid.y walks the blocks.
+__global__ __launch_bounds__(kThreads) void copy2d_kernel(const u32x4* __restrict__ src,
+                                                          long long src_pitch_vec,
+                                                          u32x4* __restrict__ dst,
+                                                          long long dst_pitch_vec, long long nvec) {
+  const long long b = blockIdx.y;
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+    dst[b * dst_pitch_vec + i] = src[b * src_pitch_vec + i];
+}
+
+inline unsigned blocks_for(long long n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+inline int log2i(long long v) {
+  int s = 0;
+  while ((1ll << s) < v) ++s;
+  return s;
+}
+
+}  // namespace
+
+int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_t heads,
+                  const void* src, void* dst, bool gather, void* stream) {
+  const long long row_vec = s.D * s.esize / 16;  // power of two (D in {64,128}, esize in {2,4})
+  const unsigned rows_out = (unsigned)(rank_count * s.chunk);
+  const long long total = (long long)rows_out * row_vec;
+  const long long bh = s.B * heads;
+  if (total == 0 || bh == 0) return 0;
+  dim3 grid(blocks_for(total), (unsigned)bh);
+  hipLaunchKernelGGL(layout_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst, s.layout == RA_ZIGZAG ? 1 : 0,
+                     (unsigned)s.cp, (unsigned)rank_begin, (unsigned)s.chunk, (unsigned)s.crow,
+                     rows_out, (unsigned)log2i(row_vec), (unsigned long long)s.S, gather ? 1 : 0);
+  return (int)hipGetLastError();
+}
+
+int launch_state_init(int64_t nrows, int64_t D, float* U, float* m, float* l, void* stream) {
+  const long long nvec = nrows * (D / 4);
+  if (nvec == 0) return 0;
+  hipLaunchKernelGGL(state_init_kernel, dim3(blocks_for(nvec)), dim3(kThreads), 0,
+                     (hipStream_t)stream, (f32x4*)U, m, l, (long long)nrows, (int)(D / 4));
+  return (int)hipGetLastError();
+}
+
+int launch_lse_merge(int64_t nrows, int64_t D, const float* o_part, const float* lse_part,
+                     float* U, float* m, float* l, void* stream) {
+  const int vs = log2i(D / 4);
+  const long long n = (long long)nrows << vs;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const f32x4*)o_part, lse_part, (f32x4*)U, m, l, (long long)nrows, vs);
+  return (int)hipGetLastError();
+}
+
+int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U, const float* m,
+                        const float* l, void* o, float* lse, void* stream) {
+  const int vs = log2i(D / 4);
+  const long long n = (long long)nrows << vs;
+  if (n == 0) return 0;
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(blocks_for(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const f32x4*)U, m, l, o, lse, (long long)nrows, vs);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(blocks_for(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const f32x4*)U, m, l, o, lse, (long long)nrows, vs);
+  return (int)hipGetLastError();
+}
+
+int launch_bwd_preprocess(int64_t nrows, int64_t D, int32_t dtype, const void* o, const void* dO,
+                          float* delta, void* stream) {
+  const long long n = nrows * 16;
+  if (n == 0) return 0;
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(preprocess_kernel<true>, dim3(blocks_for(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, o, dO, delta, (long long)nrows, (int)D);
+  else
+    hipLaunchKernelGGL(preprocess_kernel<false>, dim3(blocks_for(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, o, dO, delta, (long long)nrows, (int)D);
+  return (int)hipGetLastError();
+}
+
+int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, void* stream) {
+  const long long nvec = n / 4;
+  if (nvec == 0) return 0;
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(cast_kernel<true>, dim3(blocks_for(nvec)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const f32x4*)src, dst, nvec);
+  else
+    hipLaunchKernelGGL(cast_kernel<false>, dim3(blocks_for(nvec)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const f32x4*)src, dst, nvec);
+  return (int)hipGetLastError();
+}
+
+int launch_fill_zero(int64_t n_floats, float* dst, void* stream) {
+  const long long nvec = n_floats / 4;
+  if (nvec == 0) return 0;
+  long long nb = (nvec + kThreads - 1) / kThreads;
+  if (nb > 8192) nb = 8192;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nb), dim3(kThreads), 0, (hipStream_t)stream,
+                     (f32x4*)dst, nvec);
+  return (int)hipGetLastError();
+}
+
+int launch_copy2d(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch,
+                  int64_t block_bytes, int64_t blocks, void* stream) {
+  const long long nvec = block_bytes / 16;
+  if (nvec == 0 || blocks == 0) return 0;
+  long long gx = (nvec + kThreads - 1) / kThreads;
+  const long long cap = blocks >= 256 ? 1 : 2048 / blocks;
+  if (gx > cap) gx = cap < 1 ? 1 : cap;
+  hipLaunchKernelGGL(copy2d_kernel, dim3((unsigned)gx, (unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const u32x4*)src, (long long)(src_pitch / 16),
+                     (u32x4*)dst, (long long)(dst_pitch / 16), nvec);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ra

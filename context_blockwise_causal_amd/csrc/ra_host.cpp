@@ -1,0 +1,435 @@
+// Host driver of libringattn: the C ABI device entry points, argument validation and the
+// rank-view ring loop with side-stream staging.
+//
+// Ring on one GPU (lecture note "上下文并行", "朴素 Ring Attention" walk-through; InfiniTrain
+// "Feat: Context Parallel" 主要改动, dual compute streams with events managing cross-stream K/V
+// lifetime): at step i rank r computes with the chunk of owner (r - i) mod cp.  Step 0 uses
+// the rank's own chunk in place.  For later steps the chunk is copied into one of two
+// workspace slots on the staging stream -- the stand-in for the ring receive -- while the
+// previous step computes on the compute stream.  Event slot_ready[s] orders "copy into slot s"
+// before "compute from slot s"; event slot_free[s] orders "compute from slot s" before the next
+// copy into it.
+#include <hip/hip_runtime_api.h>
+
+#include <initializer_list>
+
+#include "ra_internal.h"
+
+struct ra_context {
+  int device;
+  hipEvent_t start;
+  hipEvent_t ready[2];
+  hipEvent_t freed[2];
+};
+
+namespace ra {
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+ra_status dev_err(int e, const char* what) {
+  if (e == 0) return RA_OK;
+  return fail(RA_ERR_DEVICE, "%s: %s", what, hipGetErrorString((hipError_t)e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+ra_status need_ptrs(std::initializer_list<const void*> ps) {
+  int i = 0;
+  for (const void* p : ps) {
+    if (!p) return fail(RA_ERR_INVALID, "pointer argument %d is NULL", i);
+    if (!aligned16(p)) return fail(RA_ERR_INVALID, "pointer argument %d is not 16-byte aligned", i);
+    ++i;
+  }
+  return RA_OK;
+}
+
+ra_status common(ra_context* ctx, const ra_problem* prob, Shape* s) {
+  clear_error();
+  if (!ctx) return fail(RA_ERR_INVALID, "context is NULL");
+  return resolve(prob, s);
+}
+
+KParams base_params(const Shape& s) {
+  KParams kp{};
+  kp.B = (int32_t)s.B;
+  kp.Hq = (int32_t)s.Hq;
+  kp.Hkv = (int32_t)s.Hkv;
+  kp.n_rep = (int32_t)s.n_rep;
+  kp.D = (int32_t)s.D;
+  kp.scale = s.scale;
+  kp.scale_log2 = s.scale * 1.4426950408889634f;
+  return kp;
+}
+
+int run_fwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream) {
+  if (s.dtype == RA_BF16) {
+    build_ranges(&kp, pairs, n, true, kFwdTileRows);
+    return kp.nranges ? launch_chunk_fwd_bf16(kp, stream) : 0;
+  }
+  build_ranges(&kp, pairs, n, true, kF32FwdTileRows);
+  return kp.nranges ? launch_chunk_fwd_f32(kp, stream) : 0;
+}
+
+int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream) {
+  if (s.dtype == RA_BF16) {
+    build_ranges(&kp, pairs, n, false, kBwdTileRows);
+    return kp.nranges ? launch_chunk_bwd_bf16(kp, stream) : 0;
+  }
+  build_ranges(&kp, pairs, n, true, kF32BwdTileRows);
+  return kp.nranges ? launch_chunk_bwd_f32(kp, stream) : 0;
+}
+
+bool any_compute(const ra_pair* pairs, int32_t n) {
+  for (int i = 0; i < n; ++i)
+    if (pairs[i].mask != RA_MASK_SKIP && pairs[i].q_len > 0 && pairs[i].kv_len > 0) return true;
+  return false;
+}
+
+// The ring loop shared by both passes.  `step_fn(step, kv_k, kv_v, kv_head_rows, owner,
+// pairs, n)` enqueues one step's compute on the compute stream.
+template <class StepFn>
+ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k_ring,
+                    const void* v_ring, char* slot0, char* slot1, hipStream_t cs, hipStream_t ss,
+                    StepFn step_fn) {
+  struct Step { int32_t i, owner, n; ra_pair pairs[4]; };
+  Step staged[64];
+  int nstaged = 0;
+  Step local{};
+  bool have_local = false;
+  // cp is bounded by the caller (<= 64 supported by this loop)
+  for (int32_t i = 0; i < s.cp; ++i) {
+    Step st{};
+    st.i = i;
+    plan_step(s, rank, i, &st.owner, st.pairs, &st.n);
+    if (!any_compute(st.pairs, st.n)) continue;
+    if (i == 0) {
+      local = st;
+      have_local = true;
+    } else {
+      staged[nstaged++] = st;
+    }
+  }
+  const int64_t row_bytes = s.D * s.esize;
+  const int64_t chunk_bytes = s.chunk * row_bytes;       // one (b, kv head) block of a chunk
+  const int64_t head_bytes = s.S * row_bytes;            // pitch of the ring tensors
+  const int64_t slot_half = s.B * s.Hkv * chunk_bytes;   // K part of a slot; V follows
+  char* slots[2] = {slot0, slot1};
+  int e;
+
+  auto issue_copy = [&](int k) -> ra_status {
+    const int sl = k & 1;
+    if (k >= 2 && (e = (int)hipStreamWaitEvent(ss, ctx->freed[sl], 0))) return dev_err(e, "wait slot_free");
+    const int64_t off = (int64_t)staged[k].owner * chunk_bytes;
+    if ((e = launch_copy2d((const char*)k_ring + off, head_bytes, slots[sl], chunk_bytes, chunk_bytes,
+                           s.B * s.Hkv, ss)))
+      return dev_err(e, "staging copy (K)");
+    if ((e = launch_copy2d((const char*)v_ring + off, head_bytes, slots[sl] + slot_half, chunk_bytes,
+                           chunk_bytes, s.B * s.Hkv, ss)))
+      return dev_err(e, "staging copy (V)");
+    if ((e = (int)hipEventRecord(ctx->ready[sl], ss))) return dev_err(e, "record slot_ready");
+    return RA_OK;
+  };
+
+  ra_status st;
+  if (nstaged > 0 && ss != cs) {
+    // The slots may still be read by earlier work on the compute stream.
+    if ((e = (int)hipEventRecord(ctx->start, cs))) return dev_err(e, "record start");
+    if ((e = (int)hipStreamWaitEvent(ss, ctx->start, 0))) return dev_err(e, "wait start");
+  }
+  if (nstaged > 0 && (st = issue_copy(0)) != RA_OK) return st;
+  if (have_local) {
+    const int64_t off = (int64_t)rank * chunk_bytes;
+    if ((e = step_fn((const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
+                     local.pairs, local.n)))
+      return dev_err(e, "chunk kernel (local step)");
+  }
+  for (int k = 0; k < nstaged; ++k) {
+    if (k + 1 < nstaged && (st = issue_copy(k + 1)) != RA_OK) return st;
+    const int sl = k & 1;
+    if ((e = (int)hipStreamWaitEvent(cs, ctx->ready[sl], 0))) return dev_err(e, "wait slot_ready");
+    if ((e = step_fn(slots[sl], slots[sl] + slot_half, s.chunk, staged[k].owner, staged[k].pairs,
+                     staged[k].n)))
+      return dev_err(e, "chunk kernel (staged step)");
+    if ((e = (int)hipEventRecord(ctx->freed[sl], cs))) return dev_err(e, "record slot_free");
+  }
+  return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+ra_status ra_create(int32_t device, ra_context** out) {
+  clear_error();
+  if (!out) return fail(RA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(RA_ERR_DEVICE, "no HIP device");
+  if (device < 0 || device >= n) return fail(RA_ERR_INVALID, "device %d outside [0, %d)", device, n);
+  DeviceGuard g(device);
+  if (!g.ok) return fail(RA_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+  ra_context* c = new ra_context();
+  c->device = device;
+  hipError_t e = hipEventCreateWithFlags(&c->start, hipEventDisableTiming);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->freed[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    delete c;
+    return fail(RA_ERR_DEVICE, "event creation failed: %s", hipGetErrorString(e));
+  }
+  *out = c;
+  return RA_OK;
+}
+
+void ra_destroy(ra_context* c) {
+  if (!c) return;
+  DeviceGuard g(c->device);
+  (void)hipEventDestroy(c->start);
+  for (int i = 0; i < 2; ++i) {
+    (void)hipEventDestroy(c->ready[i]);
+    (void)hipEventDestroy(c->freed[i]);
+  }
+  delete c;
+}
+
+ra_status ra_layout_gather(ra_context* ctx, const ra_problem* prob, int32_t rank_begin,
+                           int32_t rank_count, int64_t heads, const void* full, void* out,
+                           void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rank_count < 1 || rank_begin < 0 || rank_begin + rank_count > s.cp)
+    return fail(RA_ERR_INVALID, "rank range [%d, %d) outside [0, %d)", rank_begin,
+                rank_begin + rank_count, s.cp);
+  if (heads != s.Hq && heads != s.Hkv) return fail(RA_ERR_INVALID, "heads must be heads_q or heads_kv");
+  if ((st = need_ptrs({full, out})) != RA_OK) return st;
+  if (rank_count * s.chunk > (int64_t)UINT32_MAX / 64)
+    return fail(RA_ERR_UNSUPPORTED, "too many rows for one layout launch");
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_layout(s, rank_begin, rank_count, heads, full, out, true, stream), "layout gather");
+}
+
+ra_status ra_layout_scatter(ra_context* ctx, const ra_problem* prob, int32_t rank_begin,
+                            int32_t rank_count, int64_t heads, const void* in, void* full,
+                            void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rank_count < 1 || rank_begin < 0 || rank_begin + rank_count > s.cp)
+    return fail(RA_ERR_INVALID, "rank range [%d, %d) outside [0, %d)", rank_begin,
+                rank_begin + rank_count, s.cp);
+  if (heads != s.Hq && heads != s.Hkv) return fail(RA_ERR_INVALID, "heads must be heads_q or heads_kv");
+  if ((st = need_ptrs({in, full})) != RA_OK) return st;
+  if (rank_count * s.chunk > (int64_t)UINT32_MAX / 64)
+    return fail(RA_ERR_UNSUPPORTED, "too many rows for one layout launch");
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_layout(s, rank_begin, rank_count, heads, in, full, false, stream), "layout scatter");
+}
+
+ra_status ra_state_init(ra_context* ctx, const ra_problem* prob, int64_t rows, float* U, float* m,
+                        float* l, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_ERR_INVALID, "rows must be >= 0");
+  if ((st = need_ptrs({U, m, l})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_state_init(s.B * s.Hq * rows, s.D, U, m, l, stream), "state init");
+}
+
+ra_status ra_chunk_fwd(ra_context* ctx, const ra_problem* prob, const void* q, int64_t q_rows,
+                       const void* k, const void* v, int64_t kv_rows, const ra_pair* pairs,
+                       int32_t n_pairs, float* U, float* m, float* l, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (q_rows < 0 || kv_rows < 0) return fail(RA_ERR_INVALID, "row counts must be >= 0");
+  if ((st = check_pairs(pairs, n_pairs, q_rows, kv_rows)) != RA_OK) return st;
+  if ((st = need_ptrs({q, k, v, U, m, l})) != RA_OK) return st;
+  KParams kp = base_params(s);
+  kp.q = q; kp.k = k; kp.v = v; kp.U = U; kp.m = m; kp.l = l;
+  kp.q_head_rows = q_rows;
+  kp.kv_head_rows = kv_rows;
+  kp.dkv_head_rows = kv_rows;
+  DeviceGuard g(ctx->device);
+  return dev_err(run_fwd(s, kp, pairs, n_pairs, stream), "chunk forward");
+}
+
+ra_status ra_lse_merge(ra_context* ctx, const ra_problem* prob, int64_t rows, const float* o_part,
+                       const float* lse_part, float* U, float* m, float* l, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_ERR_INVALID, "rows must be >= 0");
+  if ((st = need_ptrs({o_part, lse_part, U, m, l})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_lse_merge(s.B * s.Hq * rows, s.D, o_part, lse_part, U, m, l, stream), "lse merge");
+}
+
+ra_status ra_fwd_finalize(ra_context* ctx, const ra_problem* prob, int64_t rows, const float* U,
+                          const float* m, const float* l, void* o, float* lse, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_ERR_INVALID, "rows must be >= 0");
+  if ((st = need_ptrs({U, m, l, o, lse})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_fwd_finalize(s.B * s.Hq * rows, s.D, s.dtype, U, m, l, o, lse, stream),
+                 "forward finalize");
+}
+
+ra_status ra_bwd_preprocess(ra_context* ctx, const ra_problem* prob, int64_t rows, const void* o,
+                            const void* dO, float* delta, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (rows < 0) return fail(RA_ERR_INVALID, "rows must be >= 0");
+  if ((st = need_ptrs({o, dO, delta})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_bwd_preprocess(s.B * s.Hq * rows, s.D, s.dtype, o, dO, delta, stream),
+                 "backward preprocess");
+}
+
+ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* prob, const void* q, const void* dO,
+                       const float* lse, const float* delta, int64_t q_rows, const void* k,
+                       const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
+                       float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (q_rows < 0 || kv_rows < 0) return fail(RA_ERR_INVALID, "row counts must be >= 0");
+  if ((st = check_pairs(pairs, n_pairs, q_rows, kv_rows)) != RA_OK) return st;
+  if ((st = need_ptrs({q, dO, lse, delta, k, v, dq_acc, dk_acc, dv_acc})) != RA_OK) return st;
+  KParams kp = base_params(s);
+  kp.q = q; kp.dO = dO; kp.lse = lse; kp.delta = delta; kp.k = k; kp.v = v;
+  kp.U = dq_acc; kp.dk = dk_acc; kp.dv = dv_acc;
+  kp.q_head_rows = q_rows;
+  kp.kv_head_rows = kv_rows;
+  kp.dkv_head_rows = kv_rows;
+  DeviceGuard g(ctx->device);
+  return dev_err(run_bwd(s, kp, pairs, n_pairs, stream), "chunk backward");
+}
+
+ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* prob, int64_t n, const float* src,
+                           void* dst, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (n < 0 || n % 4) return fail(RA_ERR_INVALID, "n must be a non-negative multiple of 4");
+  if ((st = need_ptrs({src, dst})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_cast_from_f32(n, s.dtype, src, dst, stream), "cast");
+}
+
+ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank,
+                           const void* q_slice, const void* k_ring, const void* v_ring,
+                           void* o_slice, float* lse_slice, void* workspace,
+                           size_t workspace_bytes, void* compute, void* staging) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if ((st = check_rank(s, rank)) != RA_OK) return st;
+  if (s.cp > 64) return fail(RA_ERR_UNSUPPORTED, "cp_size above 64 is not supported by the rank view");
+  if ((st = need_ptrs({q_slice, k_ring, v_ring, o_slice, lse_slice})) != RA_OK) return st;
+  const FwdWs W = fwd_ws(s);
+  if (!workspace || !aligned16(workspace)) return fail(RA_ERR_INVALID, "workspace is NULL or misaligned");
+  if (workspace_bytes < W.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
+  char* ws = static_cast<char*>(workspace);
+  float* U = reinterpret_cast<float*>(ws + W.U);
+  float* m = reinterpret_cast<float*>(ws + W.m);
+  float* l = reinterpret_cast<float*>(ws + W.l);
+  hipStream_t cs = (hipStream_t)compute;
+  hipStream_t ss = staging ? (hipStream_t)staging : cs;
+  DeviceGuard g(ctx->device);
+  int e;
+  const int64_t rows = s.B * s.Hq * s.chunk;
+  if ((e = launch_state_init(rows, s.D, U, m, l, cs))) return dev_err(e, "state init");
+  KParams kp = base_params(s);
+  kp.q = q_slice; kp.U = U; kp.m = m; kp.l = l;
+  kp.q_head_rows = s.chunk;
+  auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
+                  const ra_pair* pairs, int32_t n) -> int {
+    (void)owner;
+    kp.k = k; kp.v = v;
+    kp.kv_head_rows = kv_head_rows;
+    kp.dkv_head_rows = kv_head_rows;
+    return run_fwd(s, kp, pairs, n, cs);
+  };
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, step)) != RA_OK)
+    return st;
+  return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
+                 "forward finalize");
+}
+
+ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank,
+                           const void* q_slice, const void* k_ring, const void* v_ring,
+                           const void* o_slice, const float* lse_slice, const void* dO_slice,
+                           void* dq_slice, void* dk_ring, void* dv_ring, void* workspace,
+                           size_t workspace_bytes, void* compute, void* staging) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if ((st = check_rank(s, rank)) != RA_OK) return st;
+  if (s.cp > 64) return fail(RA_ERR_UNSUPPORTED, "cp_size above 64 is not supported by the rank view");
+  if ((st = need_ptrs({q_slice, k_ring, v_ring, o_slice, lse_slice, dO_slice, dq_slice, dk_ring,
+                       dv_ring})) != RA_OK)
+    return st;
+  const BwdWs W = bwd_ws(s);
+  if (!workspace || !aligned16(workspace)) return fail(RA_ERR_INVALID, "workspace is NULL or misaligned");
+  if (workspace_bytes < W.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
+  char* ws = static_cast<char*>(workspace);
+  float* dq = reinterpret_cast<float*>(ws + W.dq);
+  float* dk = reinterpret_cast<float*>(ws + W.dk);
+  float* dv = reinterpret_cast<float*>(ws + W.dv);
+  float* delta = reinterpret_cast<float*>(ws + W.delta);
+  hipStream_t cs = (hipStream_t)compute;
+  hipStream_t ss = staging ? (hipStream_t)staging : cs;
+  DeviceGuard g(ctx->device);
+  int e;
+  const int64_t rows = s.B * s.Hq * s.chunk;
+  const int64_t kvel = s.B * s.Hkv * s.S * s.D;
+  if ((e = launch_fill_zero(rows * s.D, dq, cs))) return dev_err(e, "zero dq");
+  if ((e = launch_fill_zero(kvel, dk, cs))) return dev_err(e, "zero dk");
+  if ((e = launch_fill_zero(kvel, dv, cs))) return dev_err(e, "zero dv");
+  if ((e = launch_bwd_preprocess(rows, s.D, s.dtype, o_slice, dO_slice, delta, cs)))
+    return dev_err(e, "backward preprocess");
+  KParams kp = base_params(s);
+  kp.q = q_slice; kp.dO = dO_slice; kp.lse = lse_slice; kp.delta = delta; kp.U = dq;
+  kp.q_head_rows = s.chunk;
+  kp.dkv_head_rows = s.S;
+  auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
+                  const ra_pair* pairs, int32_t n) -> int {
+    kp.k = k; kp.v = v;
+    kp.kv_head_rows = kv_head_rows;
+    // gradients of owner o's chunk go to its rows of the ring-ordered accumulators
+    kp.dk = dk + (int64_t)owner * s.chunk * s.D;
+    kp.dv = dv + (int64_t)owner * s.chunk * s.D;
+    return run_bwd(s, kp, pairs, n, cs);
+  };
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, step)) != RA_OK)
+    return st;
+  if ((e = launch_cast_from_f32(rows * s.D, s.dtype, dq, dq_slice, cs))) return dev_err(e, "cast dq");
+  if ((e = launch_cast_from_f32(kvel, s.dtype, dk, dk_ring, cs))) return dev_err(e, "cast dk");
+  if ((e = launch_cast_from_f32(kvel, s.dtype, dv, dv_ring, cs))) return dev_err(e, "cast dv");
+  return RA_OK;
+}
+
+}  // extern "C"

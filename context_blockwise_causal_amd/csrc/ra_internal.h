@@ -1,0 +1,118 @@
+// Internal interface between the host driver (ra_host.cpp), the planning core (ra_plan.cpp)
+// and the gfx950 kernels (kern_*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+#include "ra.h"
+
+namespace ra {
+
+// ---- error reporting (thread-local message, see ra_last_error) -------------------------
+ra_status fail(ra_status code, const char* fmt, ...);
+void clear_error();
+
+// ---- resolved problem --------------------------------------------------------------------
+struct Shape {
+  int64_t B, S, Hq, Hkv, D, n_rep;
+  int32_t cp, layout, dtype;
+  float scale;      // resolved (never 0)
+  int64_t esize;    // bytes per element of the storage dtype
+  int64_t chunk;    // rows of one rank slice, S / cp
+  int64_t nchunks;  // cp (contiguous) or 2*cp (zigzag)
+  int64_t crow;     // rows of one layout chunk, S / nchunks
+};
+
+// Validates the problem only (no rank).  Fills *out on success.
+ra_status resolve(const ra_problem* p, Shape* out);
+// Validates a rank against a resolved shape.
+ra_status check_rank(const Shape& s, int32_t rank);
+// Pair-list validation for chunk entry points (bounds, DIAG q_len == kv_len, identical or
+// disjoint Q ranges when by_q, identical or disjoint K/V ranges otherwise).
+ra_status check_pairs(const ra_pair* pairs, int32_t n, int64_t q_rows, int64_t kv_rows);
+// Plan of one ring step (always fills the SKIP pairs too).
+void plan_step(const Shape& s, int32_t rank, int32_t step, int32_t* owner, ra_pair pairs[4],
+               int32_t* n);
+// First global row of layout chunk `c`; rank r's slice holds chunk r (contiguous) or chunks
+// r and 2cp-1-r (zigzag), in that order.
+int64_t slice_chunk(const Shape& s, int32_t rank, int32_t which);
+
+// Workspace carve-up, shared by ra_workspace_size and the rank-view drivers.
+struct FwdWs { size_t U, m, l, slot[2], total; };
+struct BwdWs { size_t dq, dk, dv, delta, slot[2], total; };
+FwdWs fwd_ws(const Shape& s);
+BwdWs bwd_ws(const Shape& s);
+
+// ---- kernel parameter blocks -------------------------------------------------------------
+// A group of pairs that share one row range on the "outer" side: Q rows for the forward
+// (each workgroup owns a Q tile), K/V rows for the backward (each workgroup owns a K/V tile).
+struct KRange {
+  int64_t row0, len;      // outer rows
+  int64_t tile0, ntiles;  // first linear tile index and tile count of this range
+  int32_t npairs;
+  int32_t pair[4];        // indices into KParams::pairs
+  int32_t reverse;        // visit tiles last-to-first (heaviest first)
+  int32_t pad_;
+};
+
+struct KPair {
+  int64_t q_row0, kv_row0, q_len, kv_len;
+  int32_t mask, pad_;
+};
+
+struct KParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  const float* lse;
+  const float* delta;
+  float* U;   // fwd state / dq_acc
+  float* m;
+  float* l;
+  float* dk;  // bwd accumulators
+  float* dv;
+  int64_t q_head_rows;    // head stride (rows) of q, dO, U, m, l, lse, delta, dq
+  int64_t kv_head_rows;   // head stride (rows) of k, v
+  int64_t dkv_head_rows;  // head stride (rows) of dk, dv
+  int32_t B, Hq, Hkv, n_rep, D;
+  float scale;            // softmax scale
+  float scale_log2;       // scale * log2(e)
+  int32_t nranges;
+  int64_t tiles_per_head;
+  KRange ranges[4];
+  KPair pairs[4];
+};
+
+// Builds the range table: groups non-SKIP pairs by their outer range and assigns tiles of
+// `tile_rows` rows.  by_q selects the forward grouping (Q ranges) or the backward (K/V).
+void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64_t tile_rows);
+
+// ---- launchers (kern_*.hip); all return hipError_t as int ----------------------------------
+int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
+int launch_chunk_bwd_bf16(const KParams& kp, void* stream);
+int launch_chunk_fwd_f32(const KParams& kp, void* stream);
+int launch_chunk_bwd_f32(const KParams& kp, void* stream);
+constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)
+constexpr int64_t kBwdTileRows = 128;   // K/V rows per backward workgroup (bf16 MFMA kernel)
+constexpr int64_t kF32FwdTileRows = 1;  // one row per workgroup in the fp32 path
+constexpr int64_t kF32BwdTileRows = 1;
+
+int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_t heads,
+                  const void* src, void* dst, bool gather, void* stream);
+int launch_state_init(int64_t nrows, int64_t D, float* U, float* m, float* l, void* stream);
+int launch_lse_merge(int64_t nrows, int64_t D, const float* o_part, const float* lse_part,
+                     float* U, float* m, float* l, void* stream);
+int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U, const float* m,
+                        const float* l, void* o, float* lse, void* stream);
+int launch_bwd_preprocess(int64_t nrows, int64_t D, int32_t dtype, const void* o,
+                          const void* dO, float* delta, void* stream);
+int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, void* stream);
+int launch_fill_zero(int64_t n_floats, float* dst, void* stream);
+// Copies `blocks` blocks of `block_bytes` from src (pitch src_pitch) to dst (pitch dst_pitch).
+int launch_copy2d(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch,
+                  int64_t block_bytes, int64_t blocks, void* stream);
+
+}  // namespace ra

@@ -1,0 +1,222 @@
+/*
+ * ra.h -- C ABI of libringattn: one context-parallel rank's share of blockwise causal
+ * self-attention (the ring "p2p" mode), on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *  - Ring attention, p2p mode: K/V chunks circulate around the CP ring; each step a rank
+ *    folds the chunk it holds into its running output with a single-pass online softmax,
+ *    and the backward recomputes probabilities and returns K/V gradients to the chunk's
+ *    owner.  InfiniTrain pull request "Feat: Context Parallel", section 主要改动 (main
+ *    changes), the mode table; lecture note "上下文并行", section "朴素 Ring Attention".
+ *  - Sequence layouts: contiguous (default) or zigzag head/tail pairing of 2*cp chunks
+ *    ("Feat: Context Parallel" 主要改动; "上下文并行" section "Zig-Zag Ring Attention").
+ *  - GQA: n_rep = heads_q / heads_kv; query head h reads key/value head h / n_rep, handled
+ *    inside the kernels instead of a repeated-heads copy ("Feat: Context Parallel", review
+ *    thread on the attention helper and its RepeatKVHeads gradient grouping).
+ *  - Scope: fixed-length, equally split, causal self-attention ("Feat: Context Parallel",
+ *    section 实现边界 (implementation boundary)).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are B,H,S,D contiguous with D innermost.  "rows" counts sequence positions of
+ *    one (batch, head).  Element type of q/k/v/o/dO/dq/dk/dv is problem->dtype (fp32 or
+ *    bf16); statistics (m, l, lse, delta) and accumulators are always fp32.
+ *  - Pointers: all tensor pointers are caller-owned DEVICE memory on the context's device,
+ *    16-byte aligned.  ra_problem / ra_pair pointers and out-parameters are HOST memory.
+ *    The library allocates no device memory: scratch comes from a caller workspace sized
+ *    by ra_workspace_size.
+ *  - Streams: `stream`, `compute`, `staging` are hipStream_t values passed as void*
+ *    (NULL = the legacy default stream).  All device work is enqueued asynchronously.
+ *  - Errors: every call returns ra_status and never throws or aborts across the ABI.
+ *    Arguments are validated on the host before anything is enqueued, so a call that
+ *    returns RA_ERR_INVALID / RA_ERR_UNSUPPORTED / RA_ERR_WORKSPACE enqueued nothing.
+ *    RA_ERR_DEVICE reports a HIP launch/runtime failure; faults in already-enqueued work
+ *    surface at the caller's next synchronisation.  ra_last_error() gives a thread-local
+ *    human-readable message for the last failing call on the calling thread.
+ */
+#ifndef RINGATTN_RA_H
+#define RINGATTN_RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID = 1,      /* bad argument: shape, pointer, alignment, rank, pair list */
+  RA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype) */
+  RA_ERR_DEVICE = 3,       /* HIP runtime / launch failure */
+  RA_ERR_WORKSPACE = 4     /* workspace too small */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+typedef enum { RA_CONTIGUOUS = 0, RA_ZIGZAG = 1 } ra_layout;
+
+/* Mask kind of one (Q block, K/V block) pair.
+ *  FULL: every key visible to every query (the K/V block lies wholly in the past).
+ *  DIAG: q_len == kv_len and local key j is visible to local query i iff j <= i.
+ *  SKIP: no key visible; the pair is a no-op. */
+typedef enum { RA_MASK_FULL = 0, RA_MASK_DIAG = 1, RA_MASK_SKIP = 2 } ra_mask;
+
+/* The full-sequence problem.  Rank r's Q slice has seq_len / cp_size rows. */
+typedef struct {
+  int64_t batch;
+  int64_t seq_len;    /* full sequence length S */
+  int64_t heads_q;
+  int64_t heads_kv;   /* heads_q % heads_kv == 0 */
+  int64_t head_dim;   /* 64 or 128 */
+  int32_t cp_size;    /* simulated context-parallel degree, >= 1 */
+  int32_t layout;     /* ra_layout */
+  int32_t dtype;      /* ra_dtype */
+  float scale;        /* softmax scale; 0 selects 1/sqrt(head_dim) */
+} ra_problem;
+
+/* One pair: Q rows [q_row0, q_row0+q_len) of the Q operand against K/V rows
+ * [kv_row0, kv_row0+kv_len) of the K/V operand, with a mask kind. */
+typedef struct {
+  int64_t q_row0;
+  int64_t kv_row0;
+  int64_t q_len;
+  int64_t kv_len;
+  int32_t mask;       /* ra_mask */
+  int32_t reserved;   /* must be 0 */
+} ra_pair;
+
+typedef struct ra_context ra_context;
+
+/* ---- host-only helpers (no GPU needed) ------------------------------------------------ */
+
+const char* ra_version(void);
+const char* ra_status_str(int32_t status);
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* ra_last_error(void);
+
+/* Checks the problem and a rank: heads_q % heads_kv == 0, seq_len % cp_size == 0 (and
+ * % (2*cp_size) for zigzag), 0 <= rank < cp_size, positive sizes, a known dtype/layout.
+ * head_dim outside {64,128} returns RA_ERR_UNSUPPORTED. */
+ra_status ra_validate(const ra_problem* problem, int32_t rank);
+
+/* Ring step plan ("上下文并行", "朴素 Ring Attention": each round a rank sends its K/V to the
+ * next rank and receives the previous rank's, so at step `step` rank `rank` holds the chunk of
+ * owner (rank - step) mod cp; the zigzag per-step rule is the table in "Zig-Zag Ring
+ * Attention").  Writes the owner and up to 4 pairs (SKIP pairs included, so a plan can be
+ * audited): contiguous gives 1 pair (DIAG at step 0, FULL for 1 <= step <= rank, SKIP after);
+ * zigzag gives 4 pairs over the half-chunks (Q_lo,K_lo), (Q_lo,K_hi), (Q_hi,K_lo), (Q_hi,K_hi).
+ * q rows are offsets in the rank's Q slice, kv rows offsets in the owner's K/V chunk. */
+ra_status ra_plan_step(const ra_problem* problem, int32_t rank, int32_t step, int32_t* owner,
+                       ra_pair pairs[4], int32_t* n_pairs);
+
+/* Workspace bytes needed by ra_rank_view_fwd (pass = 0) or ra_rank_view_bwd (pass = 1). */
+ra_status ra_workspace_size(const ra_problem* problem, int32_t pass, size_t* bytes);
+
+/* ---- context ----------------------------------------------------------------------- */
+
+/* Creates a context bound to HIP device `device` (events, device properties).  The context
+ * may be used from one host thread at a time. */
+ra_status ra_create(int32_t device, ra_context** out);
+void ra_destroy(ra_context* ctx);
+
+/* ---- device entry points -------------------------------------------------------------- */
+
+/* Layout permutation ("Feat: Context Parallel" 主要改动; "上下文并行" "Zig-Zag Ring
+ * Attention"): copies, bit-exactly, the slices of ranks [rank_begin, rank_begin+rank_count)
+ * out of the full-sequence tensor `full` (batch, heads, seq_len, head_dim) into `out`
+ * (batch, heads, rank_count * seq_len/cp, head_dim), owner after owner.  rank_count = cp
+ * gives the owner-major ring order used for k_ring / v_ring; rank_count = 1 gives one rank's
+ * slice.  `heads` is heads_q or heads_kv.  ra_layout_scatter is the exact inverse (writes
+ * only the rows of those ranks into `full`). */
+ra_status ra_layout_gather(ra_context* ctx, const ra_problem* problem, int32_t rank_begin,
+                           int32_t rank_count, int64_t heads, const void* full, void* out,
+                           void* stream);
+ra_status ra_layout_scatter(ra_context* ctx, const ra_problem* problem, int32_t rank_begin,
+                            int32_t rank_count, int64_t heads, const void* in, void* full,
+                            void* stream);
+
+/* Empty online-softmax state for (batch, heads_q, rows): U = 0, m = -inf, l = 0. */
+ra_status ra_state_init(ra_context* ctx, const ra_problem* problem, int64_t rows, float* U,
+                        float* m, float* l, void* stream);
+
+/* Chunk forward ("上下文并行", "朴素 Ring Attention": safe softmax and the
+ * FlashAttention-2-style update of the output, row max and row sum per K/V block).
+ * q: (batch, heads_q, q_rows, head_dim); k, v: (batch, heads_kv, kv_rows, head_dim).
+ * State (fp32, in/out): U (batch, heads_q, q_rows, head_dim) unnormalised output,
+ * m (batch, heads_q, q_rows) row max of the scaled scores (natural-log units),
+ * l (batch, heads_q, q_rows) row sum of exp(score - m).
+ * Every non-SKIP pair is folded into its rows exactly once; pairs may share Q rows, but the
+ * Q ranges of two pairs must be identical or disjoint.  Rows no pair touches, and SKIP
+ * pairs, leave the state bit-unchanged.  bf16 path: Q K^T and P V on bf16 MFMA with fp32
+ * accumulation, P rounded to bf16 only as the MFMA operand.  fp32 path: fp32 throughout. */
+ra_status ra_chunk_fwd(ra_context* ctx, const ra_problem* problem, const void* q, int64_t q_rows,
+                       const void* k, const void* v, int64_t kv_rows, const ra_pair* pairs,
+                       int32_t n_pairs, float* U, float* m, float* l, void* stream);
+
+/* Folds an independently computed, normalised partial (o_part fp32 (batch, heads_q, rows,
+ * head_dim), lse_part fp32 (batch, heads_q, rows), -inf = empty) into the state: the partial
+ * is the state (U = o_part, m = lse_part, l = 1) ("上下文并行", "朴素 Ring Attention",
+ * order independence; Megatron's separate softmax_lse update stream in "Zig-Zag Ring
+ * Attention"). */
+ra_status ra_lse_merge(ra_context* ctx, const ra_problem* problem, int64_t rows,
+                       const float* o_part, const float* lse_part, float* U, float* m, float* l,
+                       void* stream);
+
+/* O = U / l in problem->dtype (bf16 rounded to nearest even after normalisation, per
+ * "Feat: Context Parallel" section 数值精度) and lse = m + ln l (fp32).  Rows with l = 0
+ * give O = 0 and lse = -inf. */
+ra_status ra_fwd_finalize(ra_context* ctx, const ra_problem* problem, int64_t rows,
+                          const float* U, const float* m, const float* l, void* o, float* lse,
+                          void* stream);
+
+/* delta = rowsum(dO * O) in fp32, (batch, heads_q, rows): the backward's per-row term. */
+ra_status ra_bwd_preprocess(ra_context* ctx, const ra_problem* problem, int64_t rows,
+                            const void* o, const void* dO, float* delta, void* stream);
+
+/* Chunk backward with probability recompute ("Feat: Context Parallel" 主要改动, p2p mode):
+ * for every non-SKIP pair, P = exp(scale*Q K^T - lse), dP = dO V^T, dS = P (dP - delta), and
+ *   dq_acc += scale * dS K,  dk_acc += scale * dS^T Q,  dv_acc += P^T dO  (fp32, ADDED to).
+ * q, dO: (batch, heads_q, q_rows, head_dim); lse, delta: (batch, heads_q, q_rows) fp32;
+ * k, v: (batch, heads_kv, kv_rows, head_dim); dq_acc like q, dk_acc/dv_acc like k (fp32).
+ * dk/dv of a key/value head sum the contributions of all heads_q/heads_kv query heads that
+ * read it, inside the kernel.  Accumulation uses fp32 atomics: summation order varies. */
+ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* problem, const void* q, const void* dO,
+                       const float* lse, const float* delta, int64_t q_rows, const void* k,
+                       const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
+                       float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
+
+/* Casts n fp32 values to problem->dtype (round to nearest even for bf16): the backward's
+ * final step for dQ / dK / dV accumulators. */
+ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* problem, int64_t n,
+                           const float* src, void* dst, void* stream);
+
+/* Rank-view forward: the whole ring for rank `rank` on one GPU.
+ * q_slice: the rank's Q slice (batch, heads_q, S/cp, head_dim) in slice order (see
+ * ra_layout_gather with rank_count = 1).  k_ring, v_ring: all owners' K/V in owner-major
+ * ring order (batch, heads_kv, S, head_dim) (ra_layout_gather with rank_count = cp).
+ * Outputs o_slice (like q_slice) and lse_slice (batch, heads_q, S/cp) fp32.
+ * For step i = 0..cp-1 the chunk of owner (rank - i) mod cp is copied into one of two
+ * workspace slots on `staging` (the stand-in for the ring receive) while step i-1 computes on
+ * `compute`; events order slot reuse.  A step whose pairs are all SKIP neither stages nor
+ * computes.  Workspace: ra_workspace_size(problem, 0).  compute and staging may be equal. */
+ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* problem, int32_t rank,
+                           const void* q_slice, const void* k_ring, const void* v_ring,
+                           void* o_slice, float* lse_slice, void* workspace,
+                           size_t workspace_bytes, void* compute, void* staging);
+
+/* Rank-view backward.  Inputs as for the forward plus o_slice / lse_slice from it and
+ * dO_slice (like q_slice).  Outputs dq_slice (like q_slice) and dk_ring, dv_ring
+ * (batch, heads_kv, S, head_dim) in owner-major ring order: this rank's contribution to every
+ * owner's K/V gradient (rows of chunks this rank never attends to are zero); summing dk_ring
+ * over all ranks gives the full-sequence gradient -- the ring's return-to-owner.
+ * Workspace: ra_workspace_size(problem, 1). */
+ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* problem, int32_t rank,
+                           const void* q_slice, const void* k_ring, const void* v_ring,
+                           const void* o_slice, const float* lse_slice, const void* dO_slice,
+                           void* dq_slice, void* dk_ring, void* dv_ring, void* workspace,
+                           size_t workspace_bytes, void* compute, void* staging);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_RA_H */

@@ -1,0 +1,113 @@
+"""GPU parity of the whole rank view (ring loop, staging, finalize) against the FP64 oracle at
+sizes the oracle finishes quickly, with ragged tiles, both layouts, MHA and GQA, every rank."""
+import numpy as np
+import pytest
+import torch
+
+from context_blockwise_causal_amd import api
+from context_blockwise_causal_amd.inputs import draw
+from oracle import attn64 as O
+from tests.gpu_util import assert_close, bits, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = api.Context(0)
+    yield c
+    c.close()
+
+
+def setup(ctx, B, S, Hq, Hkv, D, cp, layout, dtype, seed):
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype)
+    t = draw(B, S, Hq, Hkv, D, dtype, seed)
+    dev = {n: to_dev(t.store[n], dtype) for n in ("q", "k", "v", "do")}
+    k_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["k"])
+    v_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["v"])
+    return prob, t, dev, k_ring, v_ring
+
+
+def check_rank(ctx, prob, t, dev, k_ring, v_ring, rank, backward=True):
+    cp, layout, dtype = prob.cp, prob.layout, prob.dtype
+    q_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["q"])
+    do_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["do"])
+    o, lse = api.rank_view_fwd(ctx, prob, rank, q_sl, k_ring, v_ring,
+                               staging=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (t.as_f64(n) for n in ("q", "k", "v", "do"))
+    ro, rl = O.rank_view_fwd(q64, k64, v64, cp, layout, rank)
+    assert_close(to_f64(o), ro, dtype, f"O rank {rank}")
+    assert np.max(np.abs(to_f64(lse) - rl)) < (1e-5 if dtype == "f32" else 2e-3)
+    if not backward:
+        return
+    dq, dk_r, dv_r = api.rank_view_bwd(ctx, prob, rank, q_sl, k_ring, v_ring, o, lse, do_sl,
+                                       staging=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    pos = O.rank_positions(prob.seq_len, cp, layout, rank)
+    rdq, rdk, rdv = O.rank_view_bwd(q64, k64, v64, do64[:, :, pos], cp, layout, rank)
+    order = O.ring_order(prob.seq_len, cp, layout)
+    assert_close(to_f64(dq), rdq, dtype, f"dQ rank {rank}")
+    assert_close(to_f64(dk_r), rdk[:, :, order], dtype, f"dK rank {rank}")
+    assert_close(to_f64(dv_r), rdv[:, :, order], dtype, f"dV rank {rank}")
+
+
+CASES = [
+    # B, chunk rows, Hq, Hkv, D, cp, layout, dtype
+    (1, 200, 4, 2, 128, 1, "contiguous", "bf16"),
+    (1, 200, 4, 2, 128, 2, "contiguous", "bf16"),
+    (1, 200, 4, 2, 128, 4, "contiguous", "bf16"),
+    (1, 300, 4, 2, 128, 1, "zigzag", "bf16"),
+    (1, 300, 4, 2, 128, 2, "zigzag", "bf16"),
+    (1, 300, 4, 2, 128, 4, "zigzag", "bf16"),
+    (2, 256, 3, 3, 64, 4, "contiguous", "bf16"),
+    (2, 256, 3, 3, 64, 4, "zigzag", "bf16"),
+    (1, 80, 2, 2, 64, 2, "contiguous", "f32"),
+    (1, 80, 2, 1, 128, 2, "zigzag", "f32"),
+]
+
+
+@pytest.mark.parametrize("B,chunk,Hq,Hkv,D,cp,layout,dtype", CASES)
+def test_rank_views_match_oracle(ctx, B, chunk, Hq, Hkv, D, cp, layout, dtype):
+    S = chunk * cp
+    prob, t, dev, k_ring, v_ring = setup(ctx, B, S, Hq, Hkv, D, cp, layout, dtype, 500 + cp)
+    for rank in range(cp):
+        check_rank(ctx, prob, t, dev, k_ring, v_ring, rank)
+
+
+def test_delayed_staging_gives_identical_forward(ctx):
+    """A staging stream held back by unrelated work must not change a single output bit."""
+    prob, t, dev, k_ring, v_ring = setup(ctx, 1, 8 * 256, 4, 2, 128, 8, "zigzag", "bf16", 77)
+    q_sl = api.ra_layout_gather(ctx, prob, 7, 1, dev["q"])
+    o_ref, lse_ref = api.rank_view_fwd(ctx, prob, 7, q_sl, k_ring, v_ring)  # one stream
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big * 1e-3  # keeps the staging stream busy before the copies start
+    o, lse = api.rank_view_fwd(ctx, prob, 7, q_sl, k_ring, v_ring, staging=side)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o), bits(o_ref)) and np.array_equal(bits(lse), bits(lse_ref))
+
+
+def test_workspace_too_small_enqueues_nothing(ctx):
+    prob, t, dev, k_ring, v_ring = setup(ctx, 1, 512, 2, 2, 64, 2, "contiguous", "bf16", 5)
+    q_sl = api.ra_layout_gather(ctx, prob, 0, 1, dev["q"])
+    o = torch.zeros_like(q_sl)
+    lse = torch.zeros(1, 2, 256, device="cuda")
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        api.ra_rank_view_fwd(ctx, prob, 0, q_sl, k_ring, v_ring, o, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o.float()) == 0 and torch.count_nonzero(lse) == 0
+
+
+def test_cp1_sdpa_convenience(ctx):
+    t = draw(1, 384, 4, 2, 128, "bf16", 9)
+    q, k, v = (to_dev(t.store[n], "bf16") for n in ("q", "k", "v"))
+    o, lse = api.scaled_dot_product_attention(ctx, q, k, v, n_rep=2)
+    torch.cuda.synchronize()
+    pos = np.arange(384)
+    ro, rl = O.attention_rows(t.as_f64("q"), t.as_f64("k"), t.as_f64("v"), pos, pos)
+    assert_close(to_f64(o), ro, "bf16", "O")

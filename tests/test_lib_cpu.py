@@ -1,0 +1,99 @@
+"""CPU tests of libringattn: the library loads, exports every symbol include/ra.h declares, and
+its host-only logic (validation, ring step plans, workspace sizes) is right.  No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from context_blockwise_causal_amd import _lib as L
+from context_blockwise_causal_amd import api
+from oracle import attn64 as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KIND = {O.FULL: L.RA_MASK_FULL, O.DIAG: L.RA_MASK_DIAG, O.SKIP: L.RA_MASK_SKIP}
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_functions()
+    assert len(names) == 19
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES) | set(L.OTHER)
+    assert lib.ra_version().startswith(b"libringattn")
+    assert L.status_str(L.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("cp", [1, 2, 4, 8, 16])
+def test_plan_matches_oracle_brute_force(layout, cp):
+    S = 2 * cp * 8
+    prob = api.Problem(1, S, 2, 1, 64, cp, layout, "bf16")
+    for rank in range(cp):
+        for step in range(cp):
+            owner, pairs = api.ra_plan_step(prob, rank, step)
+            o_owner, o_pairs = O.plan_step(S, cp, layout, rank, step)
+            assert owner == o_owner
+            assert sorted(pairs) == sorted((a, b, c, d, KIND[k]) for a, b, c, d, k in o_pairs)
+
+
+def test_workspace_sizes():
+    p = api.Problem(2, 4096, 12, 4, 64, 4, "contiguous", "bf16")
+    rows = 2 * 12 * 1024
+    slot = 2 * 4 * 1024 * 64 * 2 * 2
+    assert api.ra_workspace_size(p, 0) == rows * 64 * 4 + 2 * rows * 4 + 2 * slot
+    kvel = 2 * 4 * 4096 * 64
+    assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot
+    one = api.Problem(1, 512, 2, 2, 128, 1, "contiguous", "f32")
+    assert api.ra_workspace_size(one, 0) == 2 * 512 * 128 * 4 + 2 * 4096  # no staging slots at cp=1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads_q=6, heads_kv=4), L.RA_ERR_INVALID),            # Hq % Hkv
+    (dict(seq_len=100, cp=3), L.RA_ERR_INVALID),                # S % cp
+    (dict(seq_len=96, cp=4, layout="zigzag"), L.RA_ERR_INVALID),  # S % 2cp (96 % 8 = 0 ok) -> use 100
+    (dict(head_dim=96), L.RA_ERR_UNSUPPORTED),
+    (dict(batch=0), L.RA_ERR_INVALID),
+    (dict(scale=-1.0), L.RA_ERR_INVALID),
+])
+def test_validation_errors(kw, code):
+    base = dict(batch=1, seq_len=64, heads_q=4, heads_kv=2, head_dim=64, cp=2, layout="contiguous",
+                dtype="bf16", scale=0.0)
+    base.update(kw)
+    if kw.get("layout") == "zigzag":
+        base["seq_len"] = 100  # 100 % 8 != 0
+    p = api.Problem(**base)
+    with pytest.raises(ValueError) as e:
+        api.ra_validate(p, 0)
+    assert e.value.status == code
+    assert L.last_error()
+
+
+def test_rank_and_step_errors():
+    p = api.Problem(1, 64, 2, 2, 64, 4, "zigzag", "bf16")
+    for rank in (-1, 4):
+        with pytest.raises(ValueError):
+            api.ra_validate(p, rank)
+    with pytest.raises(ValueError):
+        api.ra_plan_step(p, 0, 4)
+    bad = L.problem(1, 64, 2, 2, 64, 2, 7, L.RA_BF16)
+    assert L.load().ra_validate(ctypes.byref(bad), 0) == L.RA_ERR_INVALID
+    assert L.load().ra_validate(None, 0) == L.RA_ERR_INVALID
+
+
+def test_device_entry_points_reject_null_context_without_enqueueing():
+    p = L.problem(1, 64, 2, 2, 64, 1, L.RA_CONTIGUOUS, L.RA_BF16)
+    lib = L.load()
+    st = lib.ra_layout_gather(None, ctypes.byref(p), 0, 1, 2, None, None, None)
+    assert st == L.RA_ERR_INVALID
+    arr = L.pairs_array([(0, 0, 8, 8, L.RA_MASK_DIAG)])
+    st = lib.ra_chunk_fwd(None, ctypes.byref(p), None, 8, None, None, 8, arr, 1, None, None, None, None)
+    assert st == L.RA_ERR_INVALID
