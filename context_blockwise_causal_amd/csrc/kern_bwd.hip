@@ -249,12 +249,18 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
             dk_acc[db] = mfma32(aq, dsb[c], dk_acc[db]);
           }
         // dS to LDS as [query][key]: register 8c'+e of block qb is query qb*32 + 16c' + 8hh + e.
+        // (Elements are taken from 32-bit words: per-element extraction of a bf16 vector
+        // followed by a bit cast was observed to miscompile into repeated element-0 stores.)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 wds = __builtin_bit_cast(u32x4, dsb[c]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
+          for (int e = 0; e < 8; ++e) {
+            const unsigned wv = wds[e >> 1];
             dSs[((c >> 1) * 32 + 16 * (c & 1) + 8 * hh + e) * C::PS + kl] =
-                __builtin_bit_cast(u16, dsb[c][e]);
+                (u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+          }
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 32; ++r) dSs[(r + 32 * hh) * C::PS + kl] = 0;
