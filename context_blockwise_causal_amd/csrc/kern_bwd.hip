@@ -15,9 +15,11 @@
 //  * S = Q K^T and dP = dO V^T come out with the key index across lanes and the query index in
 //    registers (queries fed in perm32 order), which is exactly the B-operand layout that
 //    dV^T += dO^T P and dK^T += Q^T dS need; no register shuffles.
-//  * dS goes to LDS once (bf16) so that dQ = dS K (contraction over the workgroup's 128 keys)
-//    can be formed by all wavefronts, each for a 32-column slice of the head dim, and added to
-//    the fp32 dQ accumulator with coalesced 128-byte atomics.
+//  * Operands that the contraction needs transposed (Q^T, dO^T, dS, K for dQ) are read with
+//    ds_read_b64_tr_b16 out of row-major LDS tiles: two reads per 8-element operand.
+//  * dS goes to LDS once, as dS^T (bf16, 16-byte row writes), so that dQ = dS K (contraction
+//    over the workgroup's 128 keys) can be formed by all wavefronts, each for a 32-column slice
+//    of the head dim, and added to the fp32 dQ accumulator with coalesced 128-byte atomics.
 //  * dK / dV of one key/value head receive the contributions of all heads_q / heads_kv query
 //    heads through fp32 atomics at the end of each workgroup (the GQA group sum in-kernel).
 #include "kern_common.h"
@@ -32,16 +34,16 @@ constexpr int kBQ = 64;   // query rows per iteration
 template <int D>
 struct BwdCfg {
   static constexpr int P = D + 8;       // Q / dO tile pitch (elements)
-  static constexpr int PS = kBN + 8;    // dS tile pitch (elements)
+  static constexpr int PT = kBQ + 8;    // dS^T tile pitch (elements): [key][query]
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int VROW = D / 8;
   static constexpr int LOADS = kBQ * VROW / kNT;   // per thread per tile, per tensor
   static constexpr int QT = kBQ * P;               // elements of one Q (or dO) tile
-  // [Q buf0 | Q buf1 | dO buf0 | dO buf1 | dS] u16, then [lse2 x2 | delta x2] fp32
+  // [Q buf0 | Q buf1 | dO buf0 | dO buf1 | dS^T] u16, then [lse2 x2 | delta x2] fp32
   static constexpr int OFF_DO = 2 * QT;
   static constexpr int OFF_DS = 4 * QT;
-  static constexpr int U16_ELEMS = 4 * QT + kBQ * PS;
+  static constexpr int U16_ELEMS = 4 * QT + kBN * PT;
   static constexpr size_t LDS_BYTES = U16_ELEMS * sizeof(u16) + 4 * kBQ * sizeof(float);
   static_assert(2 * QT >= kBN * P, "the K tile used to build the dQ operand must fit in the Q buffers");
 };
@@ -146,8 +148,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < kBN / 16; ++c)
-      ktreg[c] = gather8(lds + (16 * c + 8 * hh) * C::P + 32 * dblk + lq, C::P);
+    for (int c = 0; c < kBN / 16; ++c) ktreg[c] = tr_operand(lds + 16 * c * C::P + 32 * dblk, C::P, lane);
     __syncthreads();
   }
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
       const u16* dOs = lds + C::OFF_DO + buf * C::QT;
       const float* lse2s = ldsf + buf * kBQ;
       const float* dlts = ldsf + 2 * kBQ + buf * kBQ;
-      u16* dSs = lds + C::OFF_DS;
+      u16* dSt = lds + C::OFF_DS;  // dS^T [key][query]
 
       // Whole wavefront in the future of every query of this tile (diagonal pairs only).
       const bool active = !(diag && kloc0 + 32 * w > qbase + kBQ - 1);
@@ -238,42 +239,36 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
           pb[c] = a;
           dsb[c] = b;
         }
-        // dV^T += dO^T P and dK^T += Q^T dS; A operands gathered down the tile's columns.
+        // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the row-major
+        // Q / dO tiles.
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bf16x8 ado = gather8(dOs + (16 * c + 8 * hh) * C::P + 32 * db + lq, C::P);
+            const bf16x8 ado = tr_operand(dOs + 16 * c * C::P + 32 * db, C::P, lane);
             dv_acc[db] = mfma32(ado, pb[c], dv_acc[db]);
-            const bf16x8 aq = gather8(Qs + (16 * c + 8 * hh) * C::P + 32 * db + lq, C::P);
+            const bf16x8 aq = tr_operand(Qs + 16 * c * C::P + 32 * db, C::P, lane);
             dk_acc[db] = mfma32(aq, dsb[c], dk_acc[db]);
           }
-        // dS to LDS as [query][key]: register 8c'+e of block qb is query qb*32 + 16c' + 8hh + e.
-        // (Elements are taken from 32-bit words: per-element extraction of a bf16 vector
-        // followed by a bit cast was observed to miscompile into repeated element-0 stores.)
+        // dS^T to LDS: register block c holds queries 16c + 8hh + 0..7 of this lane's key,
+        // one 16-byte row segment of dS^T[key][query].
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 wds = __builtin_bit_cast(u32x4, dsb[c]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const unsigned wv = wds[e >> 1];
-            dSs[((c >> 1) * 32 + 16 * (c & 1) + 8 * hh + e) * C::PS + kl] =
-                (u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
-          }
-        }
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<bf16x8*>(dSt + kl * C::PT + 16 * c + 8 * hh) = dsb[c];
       } else {
 #pragma unroll
-        for (int r = 0; r < 32; ++r) dSs[(r + 32 * hh) * C::PS + kl] = 0;
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<u32x4*>(dSt + kl * C::PT + 16 * c + 8 * hh) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
 
-      // dQ[query][32*dblk + lq] += scale * sum over the tile's 128 keys of dS * K.
+      // dQ[query][32*dblk + lq] += scale * sum over the tile's 128 keys of dS * K; the A operand
+      // dS (query x key) is read transposed out of dS^T.
       for (int qb = qb_lo; qb < qb_hi; ++qb) {
         f32x16 acc = f32x16{};
-        const u16* arow = dSs + (qb * 32 + lq) * C::PS + 8 * hh;
 #pragma unroll
         for (int c = 0; c < kBN / 16; ++c)
-          acc = mfma32(*reinterpret_cast<const bf16x8*>(arow + 16 * c), ktreg[c], acc);
+          acc = mfma32(tr_operand(dSt + 16 * c * C::PT + 32 * qb, C::PT, lane), ktreg[c], acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t q = qbase + qb * 32 + out_row(r, hh);

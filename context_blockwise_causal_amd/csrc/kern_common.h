@@ -61,6 +61,32 @@ __device__ __forceinline__ bf16x8 gather8(const u16* p, int pitch) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i, element e is
+// element (i % 4) of the 8-byte chunk addressed by lane 4*e + i/4 of the group.  Pointing lane
+// j of a group at row (k0 + j/4), column (m0 + 4*(j%4)) of a row-major tile therefore hands
+// lane i the column entries T[k0 + e][m0 + i], e = 0..3: a transposed read.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+typedef __attribute__((address_space(3))) u16 lds_u16_t;
+
+__device__ __forceinline__ v4i16 ds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_u16_t*)(p)));
+}
+
+// MFMA operand (A or B of 32x32x16) taken transposed from a row-major LDS tile T whose rows
+// run along the operand's K index and whose columns run along its M (or N) index: lane l
+// receives T[8*(l/32) + e][l % 32], e = 0..7.  T points at element [k0][m0]; pitch in
+// elements (a multiple of 4).
+__device__ __forceinline__ bf16x8 tr_operand(const u16* T, int pitch, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const u16* p = T + (8 * (g >> 1) + (j >> 2)) * pitch + 16 * (g & 1) + 4 * (j & 3);
+  const v4i16 lo = ds_read_tr16(p);
+  const v4i16 hi = ds_read_tr16(p + 4 * pitch);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 struct TileRef {
   int b, hq, g, range;
   int64_t row0;  // first outer row of the tile (in the operand's rows)

@@ -17,7 +17,10 @@
 //    per-query rescale factor is one scalar per lane.
 //  * K/V tiles of 64 keys are staged in LDS (double buffered, 16-byte coalesced global loads,
 //    prefetched into registers one tile ahead), shared by the 4 wavefronts.
-//  * exp2 with the softmax scale folded into log2(e): p = 2^(s*scale*log2e - m2).
+//  * exp2 with the softmax scale folded into log2(e): p = 2^(s*scale*log2e - m2), one FMA.
+//  * Lazy rescaling: the per-row reference m2 only moves when a tile's max exceeds it by more
+//    than 2^8, so the O^T rescale (D/2 multiplies per lane) is skipped on almost every tile.
+//  * V^T is read with ds_read_b64_tr_b16 out of the row-major V tile.
 #include "kern_common.h"
 
 namespace ra {
@@ -26,6 +29,7 @@ namespace {
 constexpr int kNT = 256;  // threads per workgroup
 constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per K/V tile
+constexpr float kLazyLog2 = 8.0f;  // allowed growth of a row max before U and l are rescaled
 
 template <int D>
 struct FwdCfg {
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float v = s[kb][r] * p.scale_log2;
+            float v = s[kb][r];
             if (edge) {
               const int64_t kj = kbase + kb * 32 + perm_reg_row(r, hh);
               if (kj >= pr.kv_len || (diag && kj > iq)) v = -__builtin_inff();
@@ -163,24 +167,30 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
             s[kb][r] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m2, mx);
-        const float base = mnew == -__builtin_inff() ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m2 - base);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+        // Lazy rescale: the reference m2 moves only when a row's tile max exceeds it by more
+        // than kLazyLog2, so exp2(score - m2) <= 2^kLazyLog2 and U, l stay consistent with m2.
+        const bool grow = mx > m2 + kLazyLog2;
+        if (__ballot(grow)) {
+          const float mnew = grow ? mx : m2;
+          const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m2 - mnew);
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+          m2 = mnew;
+        }
+        const float nbase = m2 == -__builtin_inff() ? 0.f : -m2;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[kb][r] - base);
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, nbase));
             s[kb][r] = e;
             rs += e;
           }
         rs += __shfl_xor(rs, 32);
-        lsum = lsum * alpha + rs;
-        m2 = mnew;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+        lsum += rs;
 
         // B operand P^T for key step c (16 keys): registers 8*(c&1) .. +8 of block c>>1.
         bf16x8 pb[4];
@@ -196,8 +206,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7.
-            const bf16x8 a = gather8(vt + (16 * c + 8 * hh) * C::P + 32 * db + lq, C::P);
+            // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7 (transposed read).
+            const bf16x8 a = tr_operand(vt + 16 * c * C::P + 32 * db, C::P, lane);
             oacc[db] = mfma32(a, pb[c], oacc[db]);
           }
       }
