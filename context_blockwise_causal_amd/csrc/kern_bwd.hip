@@ -16,7 +16,9 @@
 //    registers (queries fed in perm32 order), which is exactly the B-operand layout that
 //    dV^T += dO^T P and dK^T += Q^T dS need; no register shuffles.
 //  * Operands that the contraction needs transposed (Q^T, dO^T, dS, K for dQ) are read with
-//    ds_read_b64_tr_b16 out of row-major LDS tiles: two reads per 8-element operand.
+//    ds_read_b64_tr_b16 out of row-major LDS tiles: two reads per 8-element operand.  All LDS
+//    tiles are unpadded and chunk-swizzled (conflict-free row reads, transposed reads, writes).
+//  * dS is scaled by the softmax scale once, so dK and dQ need no further multiplies.
 //  * dS goes to LDS once, as dS^T (bf16, 16-byte row writes), so that dQ = dS K (contraction
 //    over the workgroup's 128 keys) can be formed by all wavefronts, each for a 32-column slice
 //    of the head dim, and added to the fp32 dQ accumulator with coalesced 128-byte atomics.
@@ -33,25 +35,23 @@ constexpr int kBQ = 64;   // query rows per iteration
 
 template <int D>
 struct BwdCfg {
-  static constexpr int P = D + 8;       // Q / dO tile pitch (elements)
-  static constexpr int PT = kBQ + 8;    // dS^T tile pitch (elements): [key][query]
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int VROW = D / 8;
-  static constexpr int LOADS = kBQ * VROW / kNT;   // per thread per tile, per tensor
-  static constexpr int QT = kBQ * P;               // elements of one Q (or dO) tile
-  // [Q buf0 | Q buf1 | dO buf0 | dO buf1 | dS^T] u16, then [lse2 x2 | delta x2] fp32
+  static constexpr int LOADS = kBQ * VROW / kNT;   // 16-byte chunks per thread per tile, per tensor
+  static constexpr int QT = kBQ * D;               // elements of one Q (or dO) tile
+  // [Q buf0 | Q buf1 | dO buf0 | dO buf1 | dS^T (kBN x kBQ)] u16, then [lse2 x2 | delta x2] fp32
   static constexpr int OFF_DO = 2 * QT;
   static constexpr int OFF_DS = 4 * QT;
-  static constexpr int U16_ELEMS = 4 * QT + kBN * PT;
+  static constexpr int U16_ELEMS = 4 * QT + kBN * kBQ;
   static constexpr size_t LDS_BYTES = U16_ELEMS * sizeof(u16) + 4 * kBQ * sizeof(float);
-  static_assert(2 * QT >= kBN * P, "the K tile used to build the dQ operand must fit in the Q buffers");
+  static_assert(2 * QT >= kBN * D, "the K tile used to build the dQ operand must fit in the Q buffers");
 };
 
 template <int D>
 __device__ __forceinline__ void load_qdo(const u16* __restrict__ Qp, const u16* __restrict__ dOp,
                                          const float* __restrict__ lse, const float* __restrict__ dlt,
-                                         int64_t q0, int64_t q_len, u32x4* qr, u32x4* dr,
+                                         int64_t q0, int64_t q_len, bool full, u32x4* qr, u32x4* dr,
                                          float* extra) {
   using C = BwdCfg<D>;
 #pragma unroll
@@ -59,7 +59,7 @@ __device__ __forceinline__ void load_qdo(const u16* __restrict__ Qp, const u16* 
     const int u = threadIdx.x + kNT * i;
     const int row = u / C::VROW, col = (u % C::VROW) * 8;
     const int64_t q = q0 + row;
-    if (q < q_len) {
+    if (full || q < q_len) {
       qr[i] = *reinterpret_cast<const u32x4*>(Qp + q * D + col);
       dr[i] = *reinterpret_cast<const u32x4*>(dOp + q * D + col);
     } else {
@@ -86,8 +86,9 @@ __device__ __forceinline__ void store_qdo(u16* __restrict__ lds, float* __restri
   for (int i = 0; i < C::LOADS; ++i) {
     const int u = threadIdx.x + kNT * i;
     const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    *reinterpret_cast<u32x4*>(lds + buf * C::QT + row * C::P + col) = qr[i];
-    *reinterpret_cast<u32x4*>(lds + C::OFF_DO + buf * C::QT + row * C::P + col) = dr[i];
+    const int off = swz_off(row, col, D);
+    *reinterpret_cast<u32x4*>(lds + buf * C::QT + off) = qr[i];
+    *reinterpret_cast<u32x4*>(lds + C::OFF_DO + buf * C::QT + off) = dr[i];
   }
   const int t = threadIdx.x;
   if (t < 2 * kBQ) {
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
   const int dblk = w % NDB;
   const int qb_lo = NDB >= 4 ? 0 : w / NDB;
   const int qb_hi = NDB >= 4 ? 2 : qb_lo + 1;
-  // B operand of dQ = dS K: lane holds K[16c + 8hh + e][32*dblk + lq] for c = 0..7.  Built
-  // once through LDS from the workgroup's K tile.
+  // B operand of dQ = dS K: lane holds K[16c + 8hh + e][32*dblk + lq] for c = 0..7, read once
+  // (transposed) from the workgroup's K tile staged in the Q buffers.
   bf16x8 ktreg[kBN / 16];
   {
     constexpr int KV = kBN * (D / 8);
@@ -144,11 +145,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
       const int row = u / (D / 8), col = (u % (D / 8)) * 8;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (row < tr.nrows) v = *reinterpret_cast<const u32x4*>(Kg + (tr.row0 + row) * D + col);
-      *reinterpret_cast<u32x4*>(lds + row * C::P + col) = v;
+      *reinterpret_cast<u32x4*>(lds + swz_off(row, col, D)) = v;
     }
     __syncthreads();
+    const TrAddr ka = make_tr_addr(lane, D);
 #pragma unroll
-    for (int c = 0; c < kBN / 16; ++c) ktreg[c] = tr_operand(lds + 16 * c * C::P + 32 * dblk, C::P, lane);
+    for (int c = 0; c < kBN / 16; ++c) ktreg[c] = tr_operand(lds, ka, D, c, dblk);
     __syncthreads();
   }
 
@@ -159,6 +161,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
     dv_acc[db] = f32x16{};
   }
 
+  // Query row fed to A-operand row lq of each 32-query block (perm32), and operand addresses.
+  const RowAddr qa0 = make_row_addr(perm32(lq), hh, D);
+  const RowAddr qa1 = make_row_addr(32 + perm32(lq), hh, D);
+  const TrAddr ta = make_tr_addr(lane, D);       // Q^T, dO^T out of the [query][d] tiles
+  const TrAddr sa = make_tr_addr(lane, kBQ);     // dS out of the dS^T [key][query] tile
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
     const KPair pr = p.pairs[R.pair[pi]];
@@ -176,19 +183,21 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
 
     u32x4 qr[C::LOADS], dr[C::LOADS];
     float extra = 0.f;
-    load_qdo<D>(Qp, dOp, lsep, dltp, q_begin, pr.q_len, qr, dr, &extra);
+    load_qdo<D>(Qp, dOp, lsep, dltp, q_begin, pr.q_len, q_begin + kBQ <= pr.q_len, qr, dr, &extra);
     store_qdo<D>(lds, ldsf, 0, qr, dr, extra);
     __syncthreads();
 
     for (int it = 0; it < niter; ++it) {
       const int buf = it & 1;
       const int64_t qbase = q_begin + (int64_t)it * kBQ;
-      if (it + 1 < niter) load_qdo<D>(Qp, dOp, lsep, dltp, qbase + kBQ, pr.q_len, qr, dr, &extra);
+      if (it + 1 < niter)
+        load_qdo<D>(Qp, dOp, lsep, dltp, qbase + kBQ, pr.q_len, qbase + 2 * kBQ <= pr.q_len, qr, dr,
+                    &extra);
       const u16* Qs = lds + buf * C::QT;
       const u16* dOs = lds + C::OFF_DO + buf * C::QT;
       const float* lse2s = ldsf + buf * kBQ;
       const float* dlts = ldsf + 2 * kBQ + buf * kBQ;
-      u16* dSt = lds + C::OFF_DS;  // dS^T [key][query]
+      u16* dSt = lds + C::OFF_DS;  // dS^T [key][query], swizzled rows of kBQ
 
       // Whole wavefront in the future of every query of this tile (diagonal pairs only).
       const bool active = !(diag && kloc0 + 32 * w > qbase + kBQ - 1);
@@ -198,12 +207,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
         for (int qb = 0; qb < 2; ++qb) {
           s[qb] = f32x16{};
           dp[qb] = f32x16{};
-          const u16* qrow = Qs + (qb * 32 + perm32(lq)) * C::P + 8 * hh;
-          const u16* drow = dOs + (qb * 32 + perm32(lq)) * C::P + 8 * hh;
 #pragma unroll
           for (int kk = 0; kk < C::KK; ++kk) {
-            s[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qrow + kk * 16), kreg[kk], s[qb]);
-            dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(drow + kk * 16), vreg[kk], dp[qb]);
+            s[qb] = mfma32(row_operand(Qs, qb ? qa1 : qa0, kk), kreg[kk], s[qb]);
+            dp[qb] = mfma32(row_operand(dOs, qb ? qa1 : qa0, kk), vreg[kk], dp[qb]);
           }
         }
         const bool edge = !kvalid || (diag && kloc0 + 32 * w + 31 > qbase);
@@ -218,13 +225,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 4 * j + i;
-              float pv = __builtin_amdgcn_exp2f(s[qb][r] * p.scale_log2 - l4[i]);
+              float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, -l4[i]));
               if (edge) {
                 const int64_t qj = qbase + r0 + i;
                 if (!kvalid || (diag && kj > qj)) pv = 0.f;
               }
               s[qb][r] = pv;
-              dp[qb][r] = pv * (dp[qb][r] - d4[i]);
+              dp[qb][r] = (pv * p.scale) * (dp[qb][r] - d4[i]);  // scale * dS
             }
           }
         bf16x8 pb[4], dsb[4];
@@ -239,40 +246,43 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
           pb[c] = a;
           dsb[c] = b;
         }
-        // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the row-major
-        // Q / dO tiles.
+        // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the Q / dO tiles.
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bf16x8 ado = tr_operand(dOs + 16 * c * C::P + 32 * db, C::P, lane);
-            dv_acc[db] = mfma32(ado, pb[c], dv_acc[db]);
-            const bf16x8 aq = tr_operand(Qs + 16 * c * C::P + 32 * db, C::P, lane);
-            dk_acc[db] = mfma32(aq, dsb[c], dk_acc[db]);
+            dv_acc[db] = mfma32(tr_operand(dOs, ta, D, c, db), pb[c], dv_acc[db]);
+            dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
-        // dS^T to LDS: register block c holds queries 16c + 8hh + 0..7 of this lane's key,
-        // one 16-byte row segment of dS^T[key][query].
+        // dS^T to LDS: register block c holds queries 16c + 8hh + 0..7 of this lane's key, one
+        // 16-byte chunk of dS^T[key][query].
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<bf16x8*>(dSt + kl * C::PT + 16 * c + 8 * hh) = dsb[c];
+          *reinterpret_cast<bf16x8*>(dSt + swz_off(kl, 16 * c + 8 * hh, kBQ)) = dsb[c];
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<u32x4*>(dSt + kl * C::PT + 16 * c + 8 * hh) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(dSt + swz_off(kl, 16 * c + 8 * hh, kBQ)) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
 
-      // dQ[query][32*dblk + lq] += scale * sum over the tile's 128 keys of dS * K; the A operand
+      // dQ[query][32*dblk + lq] += sum over the tile's 128 keys of (scale dS) * K; the A operand
       // dS (query x key) is read transposed out of dS^T.
       for (int qb = qb_lo; qb < qb_hi; ++qb) {
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int c = 0; c < kBN / 16; ++c)
-          acc = mfma32(tr_operand(dSt + 16 * c * C::PT + 32 * qb, C::PT, lane), ktreg[c], acc);
+          acc = mfma32(tr_operand(dSt, sa, kBQ, c, qb), ktreg[c], acc);
+        const int64_t q0 = qbase + qb * 32;
+        float* dst = dqp + (q0 + 4 * hh) * D + 32 * dblk + lq;
+        if (q0 + 32 <= pr.q_len) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t q = qbase + qb * 32 + out_row(r, hh);
-          if (q < pr.q_len) unsafeAtomicAdd(dqp + q * D + 32 * dblk + lq, acc[r] * p.scale);
+          for (int r = 0; r < 16; ++r)
+            unsafeAtomicAdd(dst + ((r >> 2) * 8 + (r & 3)) * D, acc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (q0 + out_row(r, hh) < pr.q_len) unsafeAtomicAdd(dst + ((r >> 2) * 8 + (r & 3)) * D, acc[r]);
         }
       }
       if (it + 1 < niter) store_qdo<D>(lds, ldsf, buf ^ 1, qr, dr, extra);
@@ -288,7 +298,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * db + out_row(r, hh);
-        unsafeAtomicAdd(dk + d, dk_acc[db][r] * p.scale);
+        unsafeAtomicAdd(dk + d, dk_acc[db][r]);
         unsafeAtomicAdd(dv + d, dv_acc[db][r]);
       }
   }

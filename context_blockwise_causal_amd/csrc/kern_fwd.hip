@@ -13,14 +13,15 @@
 //    32-key block in registers: the row max and row sum are in-register reductions plus a
 //    single exchange with the other lane half.
 //  * The output is accumulated transposed too, O^T += V^T P^T: the probabilities stay in the
-//    registers they were computed in (the K rows were fed in perm32 order for that) and the
+//    registers they were computed in (the K rows are fed in perm32 order for that) and the
 //    per-query rescale factor is one scalar per lane.
 //  * K/V tiles of 64 keys are staged in LDS (double buffered, 16-byte coalesced global loads,
-//    prefetched into registers one tile ahead), shared by the 4 wavefronts.
+//    prefetched into registers one tile ahead), shared by the 4 wavefronts.  The tiles are
+//    unpadded and chunk-swizzled, so K row reads, V^T transposed reads (ds_read_b64_tr_b16)
+//    and tile writes are free of bank conflicts.
 //  * exp2 with the softmax scale folded into log2(e): p = 2^(s*scale*log2e - m2), one FMA.
 //  * Lazy rescaling: the per-row reference m2 only moves when a tile's max exceeds it by more
 //    than 2^8, so the O^T rescale (D/2 multiplies per lane) is skipped on almost every tile.
-//  * V^T is read with ds_read_b64_tr_b16 out of the row-major V tile.
 #include "kern_common.h"
 
 namespace ra {
@@ -33,25 +34,25 @@ constexpr float kLazyLog2 = 8.0f;  // allowed growth of a row max before U and l
 
 template <int D>
 struct FwdCfg {
-  static constexpr int P = D + 8;                      // LDS row pitch (elements), 16B multiple
   static constexpr int KK = D / 16;                    // k-steps of S^T over the head dim
   static constexpr int DB = D / 32;                    // 32-row blocks of O^T
-  static constexpr int VROW = D / 8;                   // 16-byte vectors per row
-  static constexpr int LOADS = kBN * VROW / kNT;       // vectors per thread per tile, per tensor
-  static constexpr int TILE = kBN * P;                 // elements of one K (or V) LDS tile
+  static constexpr int VROW = D / 8;                   // 16-byte chunks per row
+  static constexpr int LOADS = kBN * VROW / kNT;       // chunks per thread per tile, per tensor
+  static constexpr int TILE = kBN * D;                 // elements of one K (or V) LDS tile
   static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
 };
 
 template <int D>
 __device__ __forceinline__ void load_kv(const u16* __restrict__ K, const u16* __restrict__ V,
-                                        int64_t key0, int64_t kv_len, u32x4* kr, u32x4* vr) {
+                                        int64_t key0, int64_t kv_len, bool full, u32x4* kr,
+                                        u32x4* vr) {
   using C = FwdCfg<D>;
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int u = threadIdx.x + kNT * i;
     const int row = u / C::VROW, col = (u % C::VROW) * 8;
     const int64_t key = key0 + row;
-    if (key < kv_len) {
+    if (full || key < kv_len) {
       kr[i] = *reinterpret_cast<const u32x4*>(K + key * D + col);
       vr[i] = *reinterpret_cast<const u32x4*>(V + key * D + col);
     } else {
@@ -68,8 +69,9 @@ __device__ __forceinline__ void store_kv(u16* __restrict__ buf, const u32x4* kr,
   for (int i = 0; i < C::LOADS; ++i) {
     const int u = threadIdx.x + kNT * i;
     const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    *reinterpret_cast<u32x4*>(buf + row * C::P + col) = kr[i];
-    *reinterpret_cast<u32x4*>(buf + C::TILE + row * C::P + col) = vr[i];
+    const int off = swz_off(row, col, D);
+    *reinterpret_cast<u32x4*>(buf + off) = kr[i];
+    *reinterpret_cast<u32x4*>(buf + C::TILE + off) = vr[i];
   }
 }
 
@@ -117,6 +119,10 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
       }
   }
 
+  // K row fed to A-operand row lq of each 32-key block (perm32), and the operand addresses.
+  const RowAddr ka0 = make_row_addr(perm32(lq), hh, D);
+  const RowAddr ka1 = make_row_addr(32 + perm32(lq), hh, D);
+  const TrAddr va = make_tr_addr(lane, D);
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
     const KPair pr = p.pairs[R.pair[pi]];
@@ -132,14 +138,15 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
     const bool wave_has_rows = 32 * w < tr.nrows;
 
     u32x4 kr[C::LOADS], vr[C::LOADS];
-    load_kv<D>(Kp, Vp, 0, pr.kv_len, kr, vr);
+    load_kv<D>(Kp, Vp, 0, pr.kv_len, kBN <= pr.kv_len, kr, vr);
     store_kv<D>(lds, kr, vr);
     __syncthreads();
 
     for (int kt = 0; kt < nkt; ++kt) {
       const u16* buf = lds + (kt & 1) * 2 * C::TILE;
       const int64_t kbase = (int64_t)kt * kBN;
-      if (kt + 1 < nkt) load_kv<D>(Kp, Vp, kbase + kBN, pr.kv_len, kr, vr);
+      if (kt + 1 < nkt)
+        load_kv<D>(Kp, Vp, kbase + kBN, pr.kv_len, kbase + 2 * kBN <= pr.kv_len, kr, vr);
 
       // Skip the math when the whole tile lies in the future of every query of this wave.
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
@@ -148,10 +155,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           s[kb] = f32x16{};
-          const u16* krow = buf + (kb * 32 + perm32(lq)) * C::P + 8 * hh;
 #pragma unroll
           for (int kk = 0; kk < C::KK; ++kk)
-            s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qreg[kk], s[kb]);
+            s[kb] = mfma32(row_operand(buf, kb ? ka1 : ka0, kk), qreg[kk], s[kb]);
         }
         const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
         float mx = -__builtin_inff();
@@ -205,11 +211,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < 4; ++c)
             // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7 (transposed read).
-            const bf16x8 a = tr_operand(vt + 16 * c * C::P + 32 * db, C::P, lane);
-            oacc[db] = mfma32(a, pb[c], oacc[db]);
-          }
+            oacc[db] = mfma32(tr_operand(vt, va, D, c, db), pb[c], oacc[db]);
       }
       if (kt + 1 < nkt) store_kv<D>(lds + ((kt + 1) & 1) * 2 * C::TILE, kr, vr);
       __syncthreads();
