@@ -1,4 +1,4 @@
-// Chunk backward on bf16 MFMA (gfx950) with probability recompute.
+// Chunk backward on bf16 MFMA (gfx950) with probability recompute, as two kernels.
 //
 // Method: InfiniTrain pull request "Feat: Context Parallel", section 主要改动, p2p mode: the
 // backward recomputes the probabilities from the saved log-sum-exp and returns the K/V
@@ -6,153 +6,105 @@
 //   P = exp(scale q.k - lse),  dP = dO.v,  dS = P (dP - delta),  delta = <dO, O>,
 //   dV += P^T dO,  dK += scale dS^T Q,  dQ += scale dS K.
 //
-// Layout of the work (one workgroup = 4 wavefronts = 128 keys of one (batch, query head)):
-//  * Each wavefront owns 32 keys and keeps their K and V rows in registers as MFMA operands,
-//    plus its dK^T and dV^T accumulators (fp32, 32 keys x head_dim each).
-//  * The workgroup walks the query rows of every pair that reads its keys, 64 rows at a time;
-//    the Q / dO tiles, lse and delta are staged in LDS (double buffered, prefetched one tile
-//    ahead with 16-byte loads).
-//  * S = Q K^T and dP = dO V^T come out with the key index across lanes and the query index in
-//    registers (queries fed in perm32 order), which is exactly the B-operand layout that
-//    dV^T += dO^T P and dK^T += Q^T dS need; no register shuffles.
-//  * Operands that the contraction needs transposed (Q^T, dO^T, dS, K for dQ) are read with
-//    ds_read_b64_tr_b16 out of row-major LDS tiles: two reads per 8-element operand.  All LDS
-//    tiles are unpadded and chunk-swizzled (conflict-free row reads, transposed reads, writes).
-//  * dS is scaled by the softmax scale once, so dK and dQ need no further multiplies.
-//  * dS goes to LDS once, as dS^T (bf16, 16-byte row writes), so that dQ = dS K (contraction
-//    over the workgroup's 128 keys) can be formed by all wavefronts, each for a 32-column slice
-//    of the head dim, and added to the fp32 dQ accumulator with coalesced 128-byte atomics.
-//  * dK / dV of one key/value head receive the contributions of all heads_q / heads_kv query
-//    heads through fp32 atomics at the end of each workgroup (the GQA group sum in-kernel).
+// Split: a key-major kernel forms dK and dV (each workgroup owns 128 keys and walks the query
+// rows that see them), and a query-major kernel forms dQ (each workgroup owns 128 query rows
+// and walks the keys they see).  Both recompute S and dP, which costs two extra contractions
+// over a fused kernel, but each holds at most ~230 live registers: two wavefronts per SIMD, no
+// dQ atomics, no LDS round trip of dS and one barrier per step.
+//
+// Both kernels use v_mfma_f32_32x32x16_bf16 with fp32 accumulation, LDS tiles that are
+// unpadded and chunk-swizzled (conflict-free row reads, ds_read_b64_tr_b16 transposed reads and
+// tile writes), double buffering filled by direct global->LDS loads issued one step ahead, and
+// the softmax scale folded into dS so that dK and dQ need no further multiplies.
 #include "kern_common.h"
 
 namespace ra {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kBN = 128;  // keys per workgroup
-constexpr int kBQ = 64;   // query rows per iteration
+
+// ======================================================================= dK / dV, key-major
+//
+// One workgroup = 4 wavefronts = 128 keys of one (batch, query head).  Wavefront w owns keys
+// 32w..32w+31: their K rows are in registers (B operand of S = Q K^T), their V rows come from
+// the workgroup's V tile in LDS (B operand of dP = dO V^T), and their dK^T / dV^T accumulators
+// (fp32, 32 keys x D) live in registers until the end, where they are added to dk / dv with
+// fp32 atomics (the query heads of one key/value head add into the same rows).
+//
+// S and dP come out with the key across lanes and 32 queries in registers (queries fed in
+// perm32 order), which is directly the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS.
+
+constexpr int kKvBN = 128;  // keys per workgroup
+constexpr int kKvBQ = 32;   // query rows per step
 
 template <int D>
-struct BwdCfg {
+struct KvCfg {
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int VROW = D / 8;
-  static constexpr int LOADS = kBQ * VROW / kNT;   // 16-byte chunks per thread per tile, per tensor
-  static constexpr int QT = kBQ * D;               // elements of one Q (or dO) tile
-  // [Q buf0 | Q buf1 | dO buf0 | dO buf1 | dS^T (kBN x kBQ)] u16, then [lse2 x2 | delta x2] fp32
-  static constexpr int OFF_DO = 2 * QT;
-  static constexpr int OFF_DS = 4 * QT;
-  static constexpr int U16_ELEMS = 4 * QT + kBN * kBQ;
-  static constexpr size_t LDS_BYTES = U16_ELEMS * sizeof(u16) + 4 * kBQ * sizeof(float);
-  static_assert(2 * QT >= kBN * D, "the K tile used to build the dQ operand must fit in the Q buffers");
+  static constexpr int QT = kKvBQ * D;              // elements of one Q (or dO) tile
+  // [V tile (kKvBN x D) | Q buf0 | Q buf1 | dO buf0 | dO buf1] u16, then [lse2 x2 | delta x2]
+  static constexpr int OFF_Q = kKvBN * D;
+  static constexpr int OFF_DO = OFF_Q + 2 * QT;
+  static constexpr int U16_ELEMS = OFF_DO + 2 * QT;
+  static constexpr size_t LDS_BYTES = U16_ELEMS * sizeof(u16) + 4 * kKvBQ * sizeof(float);
 };
 
-template <int D>
-__device__ __forceinline__ void load_qdo(const u16* __restrict__ Qp, const u16* __restrict__ dOp,
-                                         const float* __restrict__ lse, const float* __restrict__ dlt,
-                                         int64_t q0, int64_t q_len, bool full, u32x4* qr, u32x4* dr,
-                                         float* extra) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int u = threadIdx.x + kNT * i;
-    const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    const int64_t q = q0 + row;
-    if (full || q < q_len) {
-      qr[i] = *reinterpret_cast<const u32x4*>(Qp + q * D + col);
-      dr[i] = *reinterpret_cast<const u32x4*>(dOp + q * D + col);
-    } else {
-      qr[i] = u32x4{0u, 0u, 0u, 0u};
-      dr[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // threads 0..63 fetch lse (pre-scaled to base 2; +inf for rows outside the pair so that
-  // their probabilities are 0), threads 64..127 fetch delta.
+// lse (base 2; +inf outside the pair, so probabilities vanish there) for threads 0..31 and delta
+// for threads 32..63 of the next query step, through one register.
+__device__ __forceinline__ void kv_load_extra(const float* __restrict__ lse, const float* __restrict__ dlt,
+                                              int64_t q0, int64_t q_len, float* extra) {
   const int t = threadIdx.x;
-  if (t < 2 * kBQ) {
-    const int row = t & (kBQ - 1);
+  if (t < 2 * kKvBQ) {
+    const int row = t & (kKvBQ - 1);
     const int64_t q = q0 + row;
-    if (t < kBQ) *extra = q < q_len ? lse[q] * kLog2e : __builtin_inff();
+    if (t < kKvBQ) *extra = q < q_len ? lse[q] * kLog2e : __builtin_inff();
     else *extra = q < q_len ? dlt[q] : 0.f;
   }
 }
 
+// Q and dO rows of one query step straight into LDS (rows past the pair repeat its last row;
+// their probabilities are zero through lse = +inf).
 template <int D>
-__device__ __forceinline__ void store_qdo(u16* __restrict__ lds, float* __restrict__ ldsf, int buf,
-                                          const u32x4* qr, const u32x4* dr, float extra) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int u = threadIdx.x + kNT * i;
-    const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    const int off = swz_off(row, col, D);
-    *reinterpret_cast<u32x4*>(lds + buf * C::QT + off) = qr[i];
-    *reinterpret_cast<u32x4*>(lds + C::OFF_DO + buf * C::QT + off) = dr[i];
-  }
+__device__ __forceinline__ void kv_issue_q(const u16* __restrict__ Qp, const u16* __restrict__ dOp,
+                                           int64_t q0, int64_t q_len, u16* lds, int buf) {
+  using C = KvCfg<D>;
+  issue_tile<D, kKvBQ, 4>(Qp + q0 * D, q_len - q0, lds + C::OFF_Q + buf * C::QT);
+  issue_tile<D, kKvBQ, 4>(dOp + q0 * D, q_len - q0, lds + C::OFF_DO + buf * C::QT);
+}
+
+__device__ __forceinline__ void kv_store_extra(float* __restrict__ ldsf, int buf, float extra) {
   const int t = threadIdx.x;
-  if (t < 2 * kBQ) {
-    const int row = t & (kBQ - 1);
-    ldsf[(t < kBQ ? 0 : 2 * kBQ) + buf * kBQ + row] = extra;
+  if (t < 2 * kKvBQ) {
+    const int row = t & (kKvBQ - 1);
+    ldsf[(t < kKvBQ ? 0 : 2 * kKvBQ) + buf * kKvBQ + row] = extra;
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p) {
-  using C = BwdCfg<D>;
+__global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
+  using C = KvCfg<D>;
   extern __shared__ __attribute__((aligned(16))) u16 lds[];
-  float* ldsf = reinterpret_cast<float*>(lds + C::U16_ELEMS);  // [lse2 buf0|buf1][delta buf0|buf1]
+  float* ldsf = reinterpret_cast<float*>(lds + C::U16_ELEMS);
 
-  const TileRef tr = map_tile(p, kBN);
+  const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int kl = 32 * w + lq;  // this lane's key within the tile
   const bool kvalid = kl < tr.nrows;
   const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
   const int64_t qhead = ((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows;
   const int64_t dkvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.dkv_head_rows;
-  const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k) + kvhead * D;
-  const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v) + kvhead * D;
+  const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k) + (kvhead + tr.row0) * D;
+  const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v) + (kvhead + tr.row0) * D;
 
-  // B operands of S = Q K^T and dP = dO V^T: lane holds K/V[key][kk*16 + 8*hh .. +8].
-  bf16x8 kreg[C::KK], vreg[C::KK];
-  {
-    const int64_t krow = tr.row0 + kl;
+  // The workgroup's V tile, resident in LDS for the whole kernel (rows past the range repeat the
+  // last key; those keys are masked).
+  issue_tile<D, kKvBN, 4>(Vg, tr.nrows, lds);
+  // B operand of S = Q K^T: lane holds K[key][kk*16 + 8*hh .. +8].
+  bf16x8 kreg[C::KK];
 #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      if (kvalid) {
-        kreg[kk] = *reinterpret_cast<const bf16x8*>(Kg + krow * D + kk * 16 + 8 * hh);
-        vreg[kk] = *reinterpret_cast<const bf16x8*>(Vg + krow * D + kk * 16 + 8 * hh);
-      } else {
-        kreg[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vreg[kk] = kreg[kk];
-      }
-    }
-  }
-
-  // dQ task of this wavefront: head-dim block `dblk` for query blocks [qb_lo, qb_hi).
-  constexpr int NDB = D / 32;
-  const int dblk = w % NDB;
-  const int qb_lo = NDB >= 4 ? 0 : w / NDB;
-  const int qb_hi = NDB >= 4 ? 2 : qb_lo + 1;
-  // B operand of dQ = dS K: lane holds K[16c + 8hh + e][32*dblk + lq] for c = 0..7, read once
-  // (transposed) from the workgroup's K tile staged in the Q buffers.
-  bf16x8 ktreg[kBN / 16];
-  {
-    constexpr int KV = kBN * (D / 8);
-#pragma unroll
-    for (int i = 0; i < KV / kNT; ++i) {
-      const int u = tid + kNT * i;
-      const int row = u / (D / 8), col = (u % (D / 8)) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < tr.nrows) v = *reinterpret_cast<const u32x4*>(Kg + (tr.row0 + row) * D + col);
-      *reinterpret_cast<u32x4*>(lds + swz_off(row, col, D)) = v;
-    }
-    __syncthreads();
-    const TrAddr ka = make_tr_addr(lane, D);
-#pragma unroll
-    for (int c = 0; c < kBN / 16; ++c) ktreg[c] = tr_operand(lds, ka, D, c, dblk);
-    __syncthreads();
-  }
+  for (int kk = 0; kk < C::KK; ++kk)
+    kreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Kg + kl * D + kk * 16 + 8 * hh)
+                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
   f32x16 dk_acc[C::DB], dv_acc[C::DB];
 #pragma unroll
@@ -161,131 +113,93 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
     dv_acc[db] = f32x16{};
   }
 
-  // Query row fed to A-operand row lq of each 32-query block (perm32), and operand addresses.
-  const RowAddr qa0 = make_row_addr(perm32(lq), hh, D);
-  const RowAddr qa1 = make_row_addr(32 + perm32(lq), hh, D);
-  const TrAddr ta = make_tr_addr(lane, D);       // Q^T, dO^T out of the [query][d] tiles
-  const TrAddr sa = make_tr_addr(lane, kBQ);     // dS out of the dS^T [key][query] tile
+  const RowAddr qa = make_row_addr(perm32(lq), hh, D);  // Q / dO rows in perm32 order
+  const RowAddr va = make_row_addr(kl, hh, D);          // this lane's V row
+  const TrAddr ta = make_tr_addr(lane, D);              // Q^T, dO^T out of the [query][d] tiles
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
     const KPair pr = p.pairs[R.pair[pi]];
     const bool diag = pr.mask == RA_MASK_DIAG;
     const int64_t kloc0 = tr.row0 - pr.kv_row0;  // pair-local index of the tile's first key
     const int64_t kj = kloc0 + kl;              // pair-local index of this lane's key
-    const int64_t q_begin = diag ? (kloc0 / kBQ) * kBQ : 0;
-    const int niter = (int)((pr.q_len - q_begin + kBQ - 1) / kBQ);
+    const int64_t q_begin = diag ? (kloc0 / kKvBQ) * kKvBQ : 0;
+    const int niter = (int)((pr.q_len - q_begin + kKvBQ - 1) / kKvBQ);
     if (niter <= 0) continue;
     const u16* Qp = reinterpret_cast<const u16*>(p.q) + (qhead + pr.q_row0) * D;
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
     const float* lsep = p.lse + qhead + pr.q_row0;
     const float* dltp = p.delta + qhead + pr.q_row0;
-    float* dqp = p.U + (qhead + pr.q_row0) * D;
 
-    u32x4 qr[C::LOADS], dr[C::LOADS];
     float extra = 0.f;
-    load_qdo<D>(Qp, dOp, lsep, dltp, q_begin, pr.q_len, q_begin + kBQ <= pr.q_len, qr, dr, &extra);
-    store_qdo<D>(lds, ldsf, 0, qr, dr, extra);
+    kv_issue_q<D>(Qp, dOp, q_begin, pr.q_len, lds, 0);
+    kv_load_extra(lsep, dltp, q_begin, pr.q_len, &extra);
+    kv_store_extra(ldsf, 0, extra);
+    wait_vmem();
     __syncthreads();
 
     for (int it = 0; it < niter; ++it) {
       const int buf = it & 1;
-      const int64_t qbase = q_begin + (int64_t)it * kBQ;
-      if (it + 1 < niter)
-        load_qdo<D>(Qp, dOp, lsep, dltp, qbase + kBQ, pr.q_len, qbase + 2 * kBQ <= pr.q_len, qr, dr,
-                    &extra);
-      const u16* Qs = lds + buf * C::QT;
+      const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
+      if (it + 1 < niter) {
+        kv_issue_q<D>(Qp, dOp, qbase + kKvBQ, pr.q_len, lds, buf ^ 1);
+        kv_load_extra(lsep, dltp, qbase + kKvBQ, pr.q_len, &extra);
+      }
+      const u16* Qs = lds + C::OFF_Q + buf * C::QT;
       const u16* dOs = lds + C::OFF_DO + buf * C::QT;
-      const float* lse2s = ldsf + buf * kBQ;
-      const float* dlts = ldsf + 2 * kBQ + buf * kBQ;
-      u16* dSt = lds + C::OFF_DS;  // dS^T [key][query], swizzled rows of kBQ
+      const float* lse2s = ldsf + buf * kKvBQ;
+      const float* dlts = ldsf + 2 * kKvBQ + buf * kKvBQ;
 
-      // Whole wavefront in the future of every query of this tile (diagonal pairs only).
-      const bool active = !(diag && kloc0 + 32 * w > qbase + kBQ - 1);
+      // The whole wavefront lies in the future of every query of this step (diagonal pairs).
+      const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1);
       if (active) {
-        f32x16 s[2], dp[2];
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = f32x16{};
-          dp[qb] = f32x16{};
-#pragma unroll
-          for (int kk = 0; kk < C::KK; ++kk) {
-            s[qb] = mfma32(row_operand(Qs, qb ? qa1 : qa0, kk), kreg[kk], s[qb]);
-            dp[qb] = mfma32(row_operand(dOs, qb ? qa1 : qa0, kk), vreg[kk], dp[qb]);
-          }
+        for (int kk = 0; kk < C::KK; ++kk) {
+          s = mfma32(row_operand(Qs, qa, kk), kreg[kk], s);
+          dp = mfma32(row_operand(dOs, qa, kk), row_operand(lds, va, kk), dp);
         }
         const bool edge = !kvalid || (diag && kloc0 + 32 * w + 31 > qbase);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int j = 0; j < 4; ++j) {
+          // registers 4j..4j+3 hold queries perm_reg_row(4j+i, hh): 4 consecutive rows
+          const int r0 = perm_reg_row(4 * j, hh);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + r0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // registers 4j..4j+3 hold queries qb*32 + perm_reg_row(4j+i, hh): 4 consecutive rows
-            const int r0 = qb * 32 + perm_reg_row(4 * j, hh);
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + r0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * j + i;
-              float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.scale_log2, -l4[i]));
-              if (edge) {
-                const int64_t qj = qbase + r0 + i;
-                if (!kvalid || (diag && kj > qj)) pv = 0.f;
-              }
-              s[qb][r] = pv;
-              dp[qb][r] = (pv * p.scale) * (dp[qb][r] - d4[i]);  // scale * dS
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -l4[i]));
+            if (edge) {
+              const int64_t qj = qbase + r0 + i;
+              if (!kvalid || (diag && kj > qj)) pv = 0.f;
             }
+            s[r] = pv;
+            dp[r] = (pv * p.scale) * (dp[r] - d4[i]);  // scale * dS
           }
-        bf16x8 pb[4], dsb[4];
+        }
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
           bf16x8 a, b;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            a[e] = (__bf16)s[c >> 1][8 * (c & 1) + e];
-            b[e] = (__bf16)dp[c >> 1][8 * (c & 1) + e];
+            a[e] = (__bf16)s[8 * c + e];
+            b[e] = (__bf16)dp[8 * c + e];
           }
           pb[c] = a;
           dsb[c] = b;
         }
-        // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the Q / dO tiles.
+        // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the tiles.
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < 2; ++c) {
             dv_acc[db] = mfma32(tr_operand(dOs, ta, D, c, db), pb[c], dv_acc[db]);
             dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
-        // dS^T to LDS: register block c holds queries 16c + 8hh + 0..7 of this lane's key, one
-        // 16-byte chunk of dS^T[key][query].
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<bf16x8*>(dSt + swz_off(kl, 16 * c + 8 * hh, kBQ)) = dsb[c];
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<u32x4*>(dSt + swz_off(kl, 16 * c + 8 * hh, kBQ)) = u32x4{0u, 0u, 0u, 0u};
       }
-      __syncthreads();
-
-      // dQ[query][32*dblk + lq] += sum over the tile's 128 keys of (scale dS) * K; the A operand
-      // dS (query x key) is read transposed out of dS^T.
-      for (int qb = qb_lo; qb < qb_hi; ++qb) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int c = 0; c < kBN / 16; ++c)
-          acc = mfma32(tr_operand(dSt, sa, kBQ, c, qb), ktreg[c], acc);
-        const int64_t q0 = qbase + qb * 32;
-        float* dst = dqp + (q0 + 4 * hh) * D + 32 * dblk + lq;
-        if (q0 + 32 <= pr.q_len) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            unsafeAtomicAdd(dst + ((r >> 2) * 8 + (r & 3)) * D, acc[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (q0 + out_row(r, hh) < pr.q_len) unsafeAtomicAdd(dst + ((r >> 2) * 8 + (r & 3)) * D, acc[r]);
-        }
-      }
-      if (it + 1 < niter) store_qdo<D>(lds, ldsf, buf ^ 1, qr, dr, extra);
+      if (it + 1 < niter) kv_store_extra(ldsf, buf ^ 1, extra);
+      wait_vmem();
       __syncthreads();
     }
   }
@@ -304,27 +218,188 @@ __global__ __launch_bounds__(kNT, 1) void chunk_bwd_bf16_kernel(const KParams p)
   }
 }
 
+// ======================================================================= dQ, query-major
+//
+// One workgroup = 4 wavefronts = 128 query rows of one (batch, head); wavefront w owns 32 rows,
+// a lane one query (the forward's transposed orientation).  Per K/V tile of 64 keys:
+//   S^T = K Q^T and dP^T = V dO^T (A = K / V rows in perm32 order from LDS, B = Q / dO rows in
+//   registers), P^T = exp2(S^T scale log2e - lse2) and dS^T = scale P^T (dP^T - delta) with one
+//   lse and one delta per lane, then dQ^T += K^T dS^T (A = K^T by transposed reads, B = dS^T
+//   straight from the registers it was computed in).  The row's dQ accumulator is added to
+//   dq_acc once at the end (each row belongs to one workgroup per launch: no atomics).
+
+constexpr int kQBM = 128;  // query rows per workgroup
+constexpr int kQBN = 64;   // keys per K/V tile
+
 template <int D>
-int launch_bwd(const KParams& kp, void* stream) {
-  static bool attr_done = false;
-  const size_t lds = BwdCfg<D>::LDS_BYTES;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_bwd_bf16_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return (int)e;
-    attr_done = true;
+struct QCfg {
+  static constexpr int KK = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int TILE = kQBN * D;
+  static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
+};
+
+template <int D>
+__global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
+  using C = QCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) u16 lds[];
+
+  const TileRef tr = map_tile(p, kQBM);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int qi = 32 * w + lq;
+  const bool qvalid = qi < tr.nrows;
+  const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
+  const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
+  const u16* __restrict__ Q = reinterpret_cast<const u16*>(p.q);
+  const u16* __restrict__ dO = reinterpret_cast<const u16*>(p.dO);
+
+  // B operands: lane holds Q / dO[query][kk*16 + 8*hh .. +8]; one lse and delta per lane.
+  bf16x8 qreg[C::KK], doreg[C::KK];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) {
+    if (qvalid) {
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + kk * 16 + 8 * hh);
+      doreg[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + kk * 16 + 8 * hh);
+    } else {
+      qreg[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      doreg[kk] = qreg[kk];
+    }
   }
-  const int64_t nblk = (int64_t)kp.B * kp.Hq * kp.tiles_per_head;
-  if (nblk == 0) return 0;
-  hipLaunchKernelGGL(chunk_bwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), lds,
-                     (hipStream_t)stream, kp);
-  return (int)hipGetLastError();
+  const float nlse2 = qvalid ? -p.lse[qrow] * kLog2e : -__builtin_inff();
+  const float dl = qvalid ? p.delta[qrow] : 0.f;
+
+  // dQ^T accumulator: dq[db][4j+i] holds dQ[query][32*db + 8*j + 4*hh + i].
+  f32x16 dq[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dq[db] = f32x16{};
+
+  const RowAddr ka0 = make_row_addr(perm32(lq), hh, D);
+  const RowAddr ka1 = make_row_addr(32 + perm32(lq), hh, D);
+  const TrAddr kt = make_tr_addr(lane, D);
+  const u16* Kg = reinterpret_cast<const u16*>(p.k);
+  const u16* Vg = reinterpret_cast<const u16*>(p.v);
+  const KRange& R = p.ranges[tr.range];
+  for (int pi = 0; pi < R.npairs; ++pi) {
+    const KPair pr = p.pairs[R.pair[pi]];
+    const bool diag = pr.mask == RA_MASK_DIAG;
+    const int64_t qloc0 = tr.row0 - pr.q_row0;
+    const int64_t iq = qloc0 + qi;
+    int64_t key_end = pr.kv_len;
+    if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
+    const int nkt = (int)((key_end + kQBN - 1) / kQBN);
+    const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
+    const u16* Vp = Vg + (kvhead + pr.kv_row0) * D;
+    const int64_t wq_first = qloc0 + 32 * w;
+    const bool wave_has_rows = 32 * w < tr.nrows;
+
+    issue_tile<D, kQBN, 4>(Kp, pr.kv_len, lds);
+    issue_tile<D, kQBN, 4>(Vp, pr.kv_len, lds + C::TILE);
+    wait_vmem();
+    __syncthreads();
+
+    for (int kt_ = 0; kt_ < nkt; ++kt_) {
+      const u16* buf = lds + (kt_ & 1) * 2 * C::TILE;
+      const int64_t kbase = (int64_t)kt_ * kQBN;
+      if (kt_ + 1 < nkt) {
+        u16* nb = lds + ((kt_ + 1) & 1) * 2 * C::TILE;
+        issue_tile<D, kQBN, 4>(Kp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nb);
+        issue_tile<D, kQBN, 4>(Vp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nb + C::TILE);
+      }
+
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
+      if (active) {
+        const u16* vt = buf + C::TILE;
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+          dp[kb] = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < C::KK; ++kk) {
+            s[kb] = mfma32(row_operand(buf, kb ? ka1 : ka0, kk), qreg[kk], s[kb]);
+            dp[kb] = mfma32(row_operand(vt, kb ? ka1 : ka0, kk), doreg[kk], dp[kb]);
+          }
+        }
+        const bool edge = (kbase + kQBN > pr.kv_len) || (diag && kbase + kQBN - 1 > wq_first);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, nlse2));
+            if (edge) {
+              const int64_t kj = kbase + kb * 32 + perm_reg_row(r, hh);
+              if (kj >= pr.kv_len || (diag && kj > iq)) pv = 0.f;
+            }
+            dp[kb][r] = (pv * p.scale) * (dp[kb][r] - dl);  // scale * dS^T
+          }
+        // B operand dS^T for key step c: registers 8*(c&1) .. +8 of block c>>1.
+        bf16x8 dsb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bf16x8 t;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = (__bf16)dp[c >> 1][8 * (c & 1) + e];
+          dsb[c] = t;
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dq[db] = mfma32(tr_operand(buf, kt, D, c, db), dsb[c], dq[db]);
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (qvalid) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh);
+        f32x4 u = *dst;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] += dq[db][4 * j + i];
+        *dst = u;
+      }
+  }
+}
+
+template <class K>
+int set_lds(K kernel, size_t bytes, bool* done) {
+  if (*done) return 0;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)bytes);
+  if (e != hipSuccess) return (int)e;
+  *done = true;
+  return 0;
+}
+
+template <int D>
+int launch_bwd(const KParams& kv, const KParams& q, void* stream) {
+  static bool kv_done = false, q_done = false;
+  int e;
+  if ((e = set_lds(chunk_bwd_kv_kernel<D>, KvCfg<D>::LDS_BYTES, &kv_done))) return e;
+  if ((e = set_lds(chunk_bwd_q_kernel<D>, QCfg<D>::LDS_BYTES, &q_done))) return e;
+  const int64_t nkv = (int64_t)kv.B * kv.Hq * kv.tiles_per_head;
+  if (nkv > 0) {
+    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), KvCfg<D>::LDS_BYTES,
+                       (hipStream_t)stream, kv);
+    if ((e = (int)hipGetLastError())) return e;
+  }
+  const int64_t nq = (int64_t)q.B * q.Hq * q.tiles_per_head;
+  if (nq > 0) {
+    hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), QCfg<D>::LDS_BYTES,
+                       (hipStream_t)stream, q);
+    if ((e = (int)hipGetLastError())) return e;
+  }
+  return 0;
 }
 
 }  // namespace
 
-int launch_chunk_bwd_bf16(const KParams& kp, void* stream) {
-  return kp.D == 128 ? launch_bwd<128>(kp, stream) : launch_bwd<64>(kp, stream);
+int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream) {
+  return kv.D == 128 ? launch_bwd<128>(kv, q, stream) : launch_bwd<64>(kv, q, stream);
 }
 
 }  // namespace ra

@@ -139,6 +139,41 @@ __device__ __forceinline__ bf16x8 tr_operand(const u16* T, const TrAddr& a, int 
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Direct global -> LDS loads (global_load_lds_dwordx4): every lane copies 16 bytes from its own
+// global address to LDS at dst + 16 * lane, where dst must be wave-uniform.  The data does not
+// pass through VGPRs; completion is counted by vmcnt, so wait_vmem() followed by a barrier makes
+// a tile visible to the workgroup.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+__device__ __forceinline__ void g2lds16(const void* src, void* dst_wave) {
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)dst_wave, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Issues the loads of a swizzled ROWS x D bf16 tile whose row r comes from global row
+// g + min(r, valid_rows - 1) (valid_rows >= 1): rows past the end repeat the last valid row, so
+// every value is finite and the caller masks them out.  One wave instruction fills 1 KB of LDS,
+// i.e. 64/(D/8) whole rows; lane i lands at physical chunk i % (D/8) of its row and therefore
+// fetches the logical chunk stored there, (i % (D/8)) ^ swz(row).
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t valid_rows, u16* tile) {
+  constexpr int CH = D / 8;
+  constexpr int RPI = 64 / CH;
+  constexpr int NI = ROWS / RPI;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  static_assert(NI % NWAVES == 0, "tile rows must split evenly over the wavefronts");
+#pragma unroll
+  for (int k = 0; k < NI / NWAVES; ++k) {
+    const int i = k * NWAVES + w;
+    const int row = i * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz(row);
+    const int64_t gr = row < valid_rows ? row : valid_rows - 1;
+    g2lds16(g + gr * D + c * 8, tile + i * 512);
+  }
+}
+
 struct TileRef {
   int b, hq, g, range;
   int64_t row0;  // first outer row of the tile (in the operand's rows)

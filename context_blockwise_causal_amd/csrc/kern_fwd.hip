@@ -15,8 +15,8 @@
 //  * The output is accumulated transposed too, O^T += V^T P^T: the probabilities stay in the
 //    registers they were computed in (the K rows are fed in perm32 order for that) and the
 //    per-query rescale factor is one scalar per lane.
-//  * K/V tiles of 64 keys are staged in LDS (double buffered, 16-byte coalesced global loads,
-//    prefetched into registers one tile ahead), shared by the 4 wavefronts.  The tiles are
+//  * K/V tiles of 64 keys are staged in LDS, double buffered, shared by the 4 wavefronts, and
+//    filled by direct global->LDS loads issued one tile ahead (no VGPR staging).  The tiles are
 //    unpadded and chunk-swizzled, so K row reads, V^T transposed reads (ds_read_b64_tr_b16)
 //    and tile writes are free of bank conflicts.
 //  * exp2 with the softmax scale folded into log2(e): p = 2^(s*scale*log2e - m2), one FMA.
@@ -36,44 +36,9 @@ template <int D>
 struct FwdCfg {
   static constexpr int KK = D / 16;                    // k-steps of S^T over the head dim
   static constexpr int DB = D / 32;                    // 32-row blocks of O^T
-  static constexpr int VROW = D / 8;                   // 16-byte chunks per row
-  static constexpr int LOADS = kBN * VROW / kNT;       // chunks per thread per tile, per tensor
   static constexpr int TILE = kBN * D;                 // elements of one K (or V) LDS tile
   static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
 };
-
-template <int D>
-__device__ __forceinline__ void load_kv(const u16* __restrict__ K, const u16* __restrict__ V,
-                                        int64_t key0, int64_t kv_len, bool full, u32x4* kr,
-                                        u32x4* vr) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int u = threadIdx.x + kNT * i;
-    const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    const int64_t key = key0 + row;
-    if (full || key < kv_len) {
-      kr[i] = *reinterpret_cast<const u32x4*>(K + key * D + col);
-      vr[i] = *reinterpret_cast<const u32x4*>(V + key * D + col);
-    } else {
-      kr[i] = u32x4{0u, 0u, 0u, 0u};
-      vr[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_kv(u16* __restrict__ buf, const u32x4* kr, const u32x4* vr) {
-  using C = FwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int u = threadIdx.x + kNT * i;
-    const int row = u / C::VROW, col = (u % C::VROW) * 8;
-    const int off = swz_off(row, col, D);
-    *reinterpret_cast<u32x4*>(buf + off) = kr[i];
-    *reinterpret_cast<u32x4*>(buf + C::TILE + off) = vr[i];
-  }
-}
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p) {
@@ -137,16 +102,19 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
     const int64_t wq_first = qloc0 + 32 * w;  // pair-local index of the wavefront's first query
     const bool wave_has_rows = 32 * w < tr.nrows;
 
-    u32x4 kr[C::LOADS], vr[C::LOADS];
-    load_kv<D>(Kp, Vp, 0, pr.kv_len, kBN <= pr.kv_len, kr, vr);
-    store_kv<D>(lds, kr, vr);
+    issue_tile<D, kBN, 4>(Kp, pr.kv_len, lds);
+    issue_tile<D, kBN, 4>(Vp, pr.kv_len, lds + C::TILE);
+    wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < nkt; ++kt) {
       const u16* buf = lds + (kt & 1) * 2 * C::TILE;
       const int64_t kbase = (int64_t)kt * kBN;
-      if (kt + 1 < nkt)
-        load_kv<D>(Kp, Vp, kbase + kBN, pr.kv_len, kbase + 2 * kBN <= pr.kv_len, kr, vr);
+      if (kt + 1 < nkt) {  // next tile straight into the other buffer, overlapping this tile's math
+        u16* nb = lds + ((kt + 1) & 1) * 2 * C::TILE;
+        issue_tile<D, kBN, 4>(Kp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nb);
+        issue_tile<D, kBN, 4>(Vp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nb + C::TILE);
+      }
 
       // Skip the math when the whole tile lies in the future of every query of this wave.
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
@@ -215,7 +183,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
             // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7 (transposed read).
             oacc[db] = mfma32(tr_operand(vt, va, D, c, db), pb[c], oacc[db]);
       }
-      if (kt + 1 < nkt) store_kv<D>(lds + ((kt + 1) & 1) * 2 * C::TILE, kr, vr);
+      wait_vmem();
       __syncthreads();
     }
   }

@@ -83,8 +83,10 @@ int run_fwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* 
 
 int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream) {
   if (s.dtype == RA_BF16) {
+    KParams kq = kp;
     build_ranges(&kp, pairs, n, false, kBwdTileRows);
-    return kp.nranges ? launch_chunk_bwd_bf16(kp, stream) : 0;
+    build_ranges(&kq, pairs, n, true, kBwdQTileRows);
+    return kp.nranges ? launch_chunk_bwd_bf16(kp, kq, stream) : 0;
   }
   build_ranges(&kp, pairs, n, true, kF32BwdTileRows);
   return kp.nranges ? launch_chunk_bwd_f32(kp, stream) : 0;

@@ -92,11 +92,13 @@ void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64
 
 // ---- launchers (kern_*.hip); all return hipError_t as int ----------------------------------
 int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
-int launch_chunk_bwd_bf16(const KParams& kp, void* stream);
+// Backward as two launches: `kv` has K/V-major ranges (dK, dV), `q` Q-major ranges (dQ).
+int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
 constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)
-constexpr int64_t kBwdTileRows = 128;   // K/V rows per backward workgroup (bf16 MFMA kernel)
+constexpr int64_t kBwdTileRows = 128;   // K/V rows per dK/dV workgroup (bf16 MFMA kernel)
+constexpr int64_t kBwdQTileRows = 128;  // Q rows per dQ workgroup (bf16 MFMA kernel)
 constexpr int64_t kF32FwdTileRows = 1;  // one row per workgroup in the fp32 path
 constexpr int64_t kF32BwdTileRows = 1;
 
