@@ -74,46 +74,44 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const u16* p) {
 }
 
 // LDS tiles are stored unpadded with their 16-byte chunks XOR-swizzled per row: chunk c of
-// row r lives at chunk position c ^ swz(r).  With 32 banks x 4 bytes (128 bytes per clock)
-// this makes three access patterns conflict-free at once: 8 lanes reading one chunk from rows
-// {0,1,2,3,8,9,10,11} (row operands fed in perm32 order), 16 lanes reading 2 chunks from 4
-// aligned rows (ds_read_b64_tr_b16), and 8 lanes writing one chunk of 8 consecutive rows.
-// Rows must hold a multiple of 64 bf16 (8 chunks).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
-
-__device__ __forceinline__ int swz_off(int r, int col, int rowlen) {
-  return r * rowlen + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+// row r lives at chunk position c ^ swz(r).  The LDS has 64 banks of 4 bytes; a 16-byte read
+// serves 16 lanes per clock and an 8-byte read 32 lanes per clock (both measured).  The swizzle
+// below keeps three patterns conflict-free at once: 16 lanes reading one chunk of 16 different
+// rows (row operands, in perm32 or natural order), 32 lanes doing ds_read_b64_tr_b16 over 4
+// aligned rows x 4 chunks, and lane-linear 16-byte writes (direct global -> LDS loads).  Rows
+// hold 128 bf16 (16 chunks) or 64 bf16 (8 chunks).
+__device__ __forceinline__ int swz(int r, int rowlen) {
+  return rowlen == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Lane-constant address bases for the operand reads of a swizzled tile, so that every read in
-// an unrolled loop is one base register plus an immediate offset.
-//
+__device__ __forceinline__ int swz_off(int r, int col, int rowlen) {
+  return r * rowlen + (((col >> 3) ^ swz(r, rowlen)) << 3) + (col & 7);
+}
+
 // Row operands: lane reads T[r][16*kk + 8*hh .. +8] (r fixed per lane).  The chunk is
-// 2*kk + hh; XOR with swz(r) only touches its low 3 bits, so kk & 3 selects one of 4 bases and
-// kk >> 2 adds 64 elements.
+// 2*kk + hh = (2*kk) ^ hh, so its position is (2*kk) ^ (hh ^ swz(r)): one XOR-add per read.
 struct RowAddr {
-  int base[4];
+  int base, g8;
 };
 
 __device__ __forceinline__ RowAddr make_row_addr(int r, int hh, int rowlen) {
   RowAddr a;
-  const int s = swz(r);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) a.base[q] = r * rowlen + (((2 * q + hh) ^ s) << 3);
+  a.base = r * rowlen;
+  a.g8 = (hh ^ swz(r, rowlen)) << 3;
   return a;
 }
 
 __device__ __forceinline__ bf16x8 row_operand(const u16* T, const RowAddr& a, int kk) {
-  return *reinterpret_cast<const bf16x8*>(T + a.base[kk & 3] + 64 * (kk >> 2));
+  return *reinterpret_cast<const bf16x8*>(T + a.base + ((16 * kk) ^ a.g8));
 }
 
 // Transposed operands (ds_read_b64_tr_b16): lane l receives T[k0 + 8*(l/32) + e][m0 + l%32],
 // e = 0..7, with k0 = 16*c and m0 = 32*db.  Lane j of 16-lane group g addresses row
 // 16c + 8*(g>>1) + (j>>2) (+4 for the second read), column 32*db + 16*(g&1) + 4*(j&3).  The
-// swizzle of those rows does not depend on c, and the column chunk is 4*db + t with
-// t = 2*(g&1) + ((j&3)>>1), so db & 1 selects a base and db >> 1 adds 64 elements.
+// swizzle of those rows does not depend on c, so one address per (db, half) is precomputed and
+// c enters as an immediate offset.
 struct TrAddr {
-  int lo[2], hi[2];
+  int lo[4], hi[4];
 };
 
 __device__ __forceinline__ TrAddr make_tr_addr(int lane, int rowlen) {
@@ -123,17 +121,17 @@ __device__ __forceinline__ TrAddr make_tr_addr(int lane, int rowlen) {
   const int t = 2 * (g & 1) + ((j & 3) >> 1);
   const int within = 4 * (j & 1);
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    a.lo[par] = r * rowlen + ((((4 * par + t) ^ swz(r))) << 3) + within;
-    a.hi[par] = (r + 4) * rowlen + ((((4 * par + t) ^ swz(r + 4))) << 3) + within;
+  for (int db = 0; db < 4; ++db) {
+    a.lo[db] = r * rowlen + (((4 * db + t) ^ swz(r, rowlen)) << 3) + within;
+    a.hi[db] = (r + 4) * rowlen + (((4 * db + t) ^ swz(r + 4, rowlen)) << 3) + within;
   }
   return a;
 }
 
 __device__ __forceinline__ bf16x8 tr_operand(const u16* T, const TrAddr& a, int rowlen, int c, int db) {
-  const int off = 16 * c * rowlen + 64 * (db >> 1);
-  const v4i16 lo = ds_read_tr16(T + a.lo[db & 1] + off);
-  const v4i16 hi = ds_read_tr16(T + a.hi[db & 1] + off);
+  const int off = 16 * c * rowlen;
+  const v4i16 lo = ds_read_tr16(T + a.lo[db] + off);
+  const v4i16 hi = ds_read_tr16(T + a.hi[db] + off);
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, w);
@@ -168,7 +166,7 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t va
   for (int k = 0; k < NI / NWAVES; ++k) {
     const int i = k * NWAVES + w;
     const int row = i * RPI + lane / CH;
-    const int c = (lane % CH) ^ swz(row);
+    const int c = (lane % CH) ^ swz(row, D);
     const int64_t gr = row < valid_rows ? row : valid_rows - 1;
     g2lds16(g + gr * D + c * 8, tile + i * 512);
   }

@@ -37,13 +37,15 @@ struct FwdCfg {
   static constexpr int KK = D / 16;                    // k-steps of S^T over the head dim
   static constexpr int DB = D / 32;                    // 32-row blocks of O^T
   static constexpr int TILE = kBN * D;                 // elements of one K (or V) LDS tile
-  static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
 };
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p) {
   using C = FwdCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) u16 lds[];
+  // Two K/V buffers as four distinct LDS objects: the tile loop is unrolled by two so that every
+  // step reads one pair of objects while direct loads fill the other, and the compiler can tell
+  // that those loads do not alias the reads (no wait on them before the step's LDS reads).
+  __shared__ __attribute__((aligned(16))) u16 k0[C::TILE], v0[C::TILE], k1[C::TILE], v1[C::TILE];
 
   const TileRef tr = map_tile(p, kBM);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -102,43 +104,36 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
     const int64_t wq_first = qloc0 + 32 * w;  // pair-local index of the wavefront's first query
     const bool wave_has_rows = 32 * w < tr.nrows;
 
-    issue_tile<D, kBN, 4>(Kp, pr.kv_len, lds);
-    issue_tile<D, kBN, 4>(Vp, pr.kv_len, lds + C::TILE);
-    wait_vmem();
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-      const u16* buf = lds + (kt & 1) * 2 * C::TILE;
+    // One key tile: issue the next tile's loads into (nk, nv), then compute on (kb, vb).
+    auto step = [&](const u16* kb, const u16* vb, u16* nk, u16* nv, int kt) {
       const int64_t kbase = (int64_t)kt * kBN;
-      if (kt + 1 < nkt) {  // next tile straight into the other buffer, overlapping this tile's math
-        u16* nb = lds + ((kt + 1) & 1) * 2 * C::TILE;
-        issue_tile<D, kBN, 4>(Kp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nb);
-        issue_tile<D, kBN, 4>(Vp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nb + C::TILE);
+      if (kt + 1 < nkt) {
+        issue_tile<D, kBN, 4>(Kp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nk);
+        issue_tile<D, kBN, 4>(Vp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nv);
       }
-
       // Skip the math when the whole tile lies in the future of every query of this wave.
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
       if (active) {
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
+        for (int b = 0; b < 2; ++b) {
+          s[b] = f32x16{};
 #pragma unroll
           for (int kk = 0; kk < C::KK; ++kk)
-            s[kb] = mfma32(row_operand(buf, kb ? ka1 : ka0, kk), qreg[kk], s[kb]);
+            s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
         }
         const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float v = s[kb][r];
+            float v = s[b][r];
             if (edge) {
-              const int64_t kj = kbase + kb * 32 + perm_reg_row(r, hh);
+              const int64_t kj = kbase + b * 32 + perm_reg_row(r, hh);
               if (kj >= pr.kv_len || (diag && kj > iq)) v = -__builtin_inff();
             }
-            s[kb][r] = v;
+            s[b][r] = v;
             mx = fmaxf(mx, v);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
@@ -156,11 +151,11 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
         const float nbase = m2 == -__builtin_inff() ? 0.f : -m2;
         float rs = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, nbase));
-            s[kb][r] = e;
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[b][r], p.scale_log2, nbase));
+            s[b][r] = e;
             rs += e;
           }
         rs += __shfl_xor(rs, 32);
@@ -175,16 +170,24 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
           for (int e = 0; e < 8; ++e) t[e] = (__bf16)s[c >> 1][8 * (c & 1) + e];
           pb[c] = t;
         }
-        const u16* vt = buf + C::TILE;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             // A operand V^T: lane holds V[16c + 8hh + e][32db + lq], e = 0..7 (transposed read).
-            oacc[db] = mfma32(tr_operand(vt, va, D, c, db), pb[c], oacc[db]);
+            oacc[db] = mfma32(tr_operand(vb, va, D, c, db), pb[c], oacc[db]);
       }
       wait_vmem();
       __syncthreads();
+    };
+
+    issue_tile<D, kBN, 4>(Kp, pr.kv_len, k0);
+    issue_tile<D, kBN, 4>(Vp, pr.kv_len, v0);
+    wait_vmem();
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+      step(k0, v0, k1, v1, kt);
+      if (kt + 1 < nkt) step(k1, v1, k0, v0, kt + 1);
     }
   }
 
@@ -207,18 +210,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
 
 template <int D>
 int launch_fwd(const KParams& kp, void* stream) {
-  static bool attr_done = false;
-  const size_t lds = FwdCfg<D>::LDS_BYTES;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_fwd_bf16_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return (int)e;
-    attr_done = true;
-  }
   const int64_t nblk = (int64_t)kp.B * kp.Hq * kp.tiles_per_head;
   if (nblk == 0) return 0;
-  hipLaunchKernelGGL(chunk_fwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), lds,
-                     (hipStream_t)stream, kp);
+  hipLaunchKernelGGL(chunk_fwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), 0, (hipStream_t)stream, kp);
   return (int)hipGetLastError();
 }
 
