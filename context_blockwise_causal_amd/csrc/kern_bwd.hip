@@ -41,50 +41,45 @@ template <int D>
 struct KvCfg {
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QT = kKvBQ * D;              // elements of one Q (or dO) tile
-  // [V tile (kKvBN x D) | Q buf0 | Q buf1 | dO buf0 | dO buf1] u16, then [lse2 x2 | delta x2]
-  static constexpr int OFF_Q = kKvBN * D;
-  static constexpr int OFF_DO = OFF_Q + 2 * QT;
-  static constexpr int U16_ELEMS = OFF_DO + 2 * QT;
-  static constexpr size_t LDS_BYTES = U16_ELEMS * sizeof(u16) + 4 * kKvBQ * sizeof(float);
+  static constexpr int QT = kKvBQ * D;  // elements of one Q (or dO) tile
 };
 
-// lse (base 2; +inf outside the pair, so probabilities vanish there) for threads 0..31 and delta
-// for threads 32..63 of the next query step, through one register.
-__device__ __forceinline__ void kv_load_extra(const float* __restrict__ lse, const float* __restrict__ dlt,
-                                              int64_t q0, int64_t q_len, float* extra) {
+// lse for threads 0..31 and delta for threads 32..63 of a query step, one value per thread,
+// loaded raw (row index clamped into the pair) so that nothing waits on the load before the
+// store at the end of the step.
+__device__ __forceinline__ float kv_load_extra(const float* __restrict__ lse, const float* __restrict__ dlt,
+                                               int64_t q0, int64_t q_len) {
   const int t = threadIdx.x;
+  float x = 0.f;
   if (t < 2 * kKvBQ) {
-    const int row = t & (kKvBQ - 1);
-    const int64_t q = q0 + row;
-    if (t < kKvBQ) *extra = q < q_len ? lse[q] * kLog2e : __builtin_inff();
-    else *extra = q < q_len ? dlt[q] : 0.f;
+    const int64_t q = q0 + (t & (kKvBQ - 1));
+    x = (t < kKvBQ ? lse : dlt)[q < q_len ? q : q_len - 1];
   }
+  return x;
 }
 
-// Q and dO rows of one query step straight into LDS (rows past the pair repeat its last row;
-// their probabilities are zero through lse = +inf).
-template <int D>
-__device__ __forceinline__ void kv_issue_q(const u16* __restrict__ Qp, const u16* __restrict__ dOp,
-                                           int64_t q0, int64_t q_len, u16* lds, int buf) {
-  using C = KvCfg<D>;
-  issue_tile<D, kKvBQ, 4>(Qp + q0 * D, q_len - q0, lds + C::OFF_Q + buf * C::QT);
-  issue_tile<D, kKvBQ, 4>(dOp + q0 * D, q_len - q0, lds + C::OFF_DO + buf * C::QT);
-}
-
-__device__ __forceinline__ void kv_store_extra(float* __restrict__ ldsf, int buf, float extra) {
+// Stores the step's lse in base 2 (+inf for rows past the pair, so their probabilities vanish)
+// and delta (0 past the pair).
+__device__ __forceinline__ void kv_store_extra(float* __restrict__ ex, float x, int64_t q0, int64_t q_len) {
   const int t = threadIdx.x;
   if (t < 2 * kKvBQ) {
-    const int row = t & (kKvBQ - 1);
-    ldsf[(t < kKvBQ ? 0 : 2 * kKvBQ) + buf * kKvBQ + row] = extra;
+    const bool valid = q0 + (t & (kKvBQ - 1)) < q_len;
+    ex[t] = t < kKvBQ ? (valid ? x * kLog2e : __builtin_inff()) : (valid ? x : 0.f);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   using C = KvCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) u16 lds[];
-  float* ldsf = reinterpret_cast<float*>(lds + C::U16_ELEMS);
+  // The V tile and two buffers of (Q, dO, lse|delta), carved out of one LDS array.  Each step
+  // reads one buffer while direct loads fill the other; the step takes every LDS pointer as a
+  // __restrict__ parameter, which lets the compiler prove that those loads do not alias its reads
+  // (so it does not wait for them before the step's LDS reads).  One array, not several: with
+  // several LDS variables the compiler's LDS lowering replaces the pointer-based alias scopes.
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT + 8 * kKvBQ];
+  u16* const vt = lds;
+  u16* const qdbuf = lds + kKvBN * D;
+  float* const exbuf = reinterpret_cast<float*>(lds + kKvBN * D + 4 * C::QT);
 
   const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -98,7 +93,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 
   // The workgroup's V tile, resident in LDS for the whole kernel (rows past the range repeat the
   // last key; those keys are masked).
-  issue_tile<D, kKvBN, 4>(Vg, tr.nrows, lds);
+  issue_tile<D, kKvBN, 4>(Vg, tr.nrows, vt);
   // B operand of S = Q K^T: lane holds K[key][kk*16 + 8*hh .. +8].
   bf16x8 kreg[C::KK];
 #pragma unroll
@@ -130,25 +125,17 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const float* lsep = p.lse + qhead + pr.q_row0;
     const float* dltp = p.delta + qhead + pr.q_row0;
 
-    float extra = 0.f;
-    kv_issue_q<D>(Qp, dOp, q_begin, pr.q_len, lds, 0);
-    kv_load_extra(lsep, dltp, q_begin, pr.q_len, &extra);
-    kv_store_extra(ldsf, 0, extra);
-    wait_vmem();
-    __syncthreads();
-
-    for (int it = 0; it < niter; ++it) {
-      const int buf = it & 1;
+    // One query step on (Qs, dOs, ex); the next step's rows go into (nQ, ndO, nex).
+    auto step = [&](const u16* __restrict__ Vs, const u16* __restrict__ Qs, const u16* __restrict__ dOs,
+                    const float* __restrict__ ex, u16* __restrict__ nQ, u16* __restrict__ ndO,
+                    float* __restrict__ nex, int it) {
       const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
+      float extra = 0.f;
       if (it + 1 < niter) {
-        kv_issue_q<D>(Qp, dOp, qbase + kKvBQ, pr.q_len, lds, buf ^ 1);
-        kv_load_extra(lsep, dltp, qbase + kKvBQ, pr.q_len, &extra);
+        issue_tile<D, kKvBQ, 4>(Qp + (qbase + kKvBQ) * D, pr.q_len - qbase - kKvBQ, nQ);
+        issue_tile<D, kKvBQ, 4>(dOp + (qbase + kKvBQ) * D, pr.q_len - qbase - kKvBQ, ndO);
+        extra = kv_load_extra(lsep, dltp, qbase + kKvBQ, pr.q_len);
       }
-      const u16* Qs = lds + C::OFF_Q + buf * C::QT;
-      const u16* dOs = lds + C::OFF_DO + buf * C::QT;
-      const float* lse2s = ldsf + buf * kKvBQ;
-      const float* dlts = ldsf + 2 * kKvBQ + buf * kKvBQ;
-
       // The whole wavefront lies in the future of every query of this step (diagonal pairs).
       const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1);
       if (active) {
@@ -156,9 +143,14 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
           s = mfma32(row_operand(Qs, qa, kk), kreg[kk], s);
-          dp = mfma32(row_operand(dOs, qa, kk), row_operand(lds, va, kk), dp);
+          dp = mfma32(row_operand(dOs, qa, kk), row_operand(Vs, va, kk), dp);
         }
+        // Excluded (key, query) pairs: keys past the range, and keys after the query in a
+        // diagonal pair.  Only steps on an edge take the masked path.
         const bool edge = !kvalid || (diag && kloc0 + 32 * w + 31 > qbase);
+        const int qmin = edge ? (kvalid ? (int)(kj - qbase) : 1 << 20) : -1;  // first visible query
+        const float* lse2s = ex;
+        const float* dlts = ex + kKvBQ;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // registers 4j..4j+3 hold queries perm_reg_row(4j+i, hh): 4 consecutive rows
@@ -169,10 +161,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
             float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -l4[i]));
-            if (edge) {
-              const int64_t qj = qbase + r0 + i;
-              if (!kvalid || (diag && kj > qj)) pv = 0.f;
-            }
+            pv = (r0 + i < qmin) ? 0.f : pv;
             s[r] = pv;
             dp[r] = (pv * p.scale) * (dp[r] - d4[i]);  // scale * dS
           }
@@ -198,23 +187,54 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
             dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
       }
-      if (it + 1 < niter) kv_store_extra(ldsf, buf ^ 1, extra);
+      if (it + 1 < niter) kv_store_extra(nex, extra, qbase + kKvBQ, pr.q_len);
       wait_vmem();
       __syncthreads();
+    };
+
+    issue_tile<D, kKvBQ, 4>(Qp + q_begin * D, pr.q_len - q_begin, qdbuf);
+    issue_tile<D, kKvBQ, 4>(dOp + q_begin * D, pr.q_len - q_begin, qdbuf + C::QT);
+    kv_store_extra(exbuf, kv_load_extra(lsep, dltp, q_begin, pr.q_len), q_begin, pr.q_len);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < niter; ++it) {
+      u16* cur = qdbuf + (it & 1) * 2 * C::QT;
+      u16* nxt = qdbuf + ((it + 1) & 1) * 2 * C::QT;
+      float* ecur = exbuf + (it & 1) * 2 * kKvBQ;
+      float* enxt = exbuf + ((it + 1) & 1) * 2 * kKvBQ;
+      step(vt, cur, cur + C::QT, ecur, nxt, nxt + C::QT, enxt, it);
     }
   }
 
-  if (kvalid) {
-    float* dk = p.dk + (dkvhead + tr.row0 + kl) * D;
-    float* dv = p.dv + (dkvhead + tr.row0 + kl) * D;
+  // The query heads of one key/value head add into the same dK/dV rows, so the sums go out as
+  // fp32 atomics.  The accumulators hold one key per lane; written as they are, every atomic
+  // instruction would touch 64 rows.  Each wavefront therefore stages its 32 x D block in LDS
+  // (16-byte chunks XOR-swizzled by row, conflict-free both ways) and adds it back row by row,
+  // 64 consecutive floats per instruction.
+  wait_vmem();
+  __syncthreads();
+  float* const st = reinterpret_cast<float*>(lds) + w * (32 * D);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const f32x16* acc = t ? dv_acc : dk_acc;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + out_row(r, hh);
-        unsafeAtomicAdd(dk + d, dk_acc[db][r]);
-        unsafeAtomicAdd(dv + d, dv_acc[db][r]);
+      for (int j = 0; j < 4; ++j) {
+        // registers 4j..4j+3 hold d = 32 db + 8 j + 4 hh + (0..3): chunk 8 db + 2 j + hh
+        const int c = 8 * db + 2 * j + hh;
+        *reinterpret_cast<f32x4*>(st + lq * D + ((c ^ (lq & 15)) << 2)) =
+            f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
       }
+    float* const g = (t ? p.dv : p.dk) + (dkvhead + tr.row0 + 32 * w) * D;
+    for (int k = 0; k < 32; ++k) {
+      if (32 * w + k >= tr.nrows) break;
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) {
+        const int d = 64 * h + lane;
+        unsafeAtomicAdd(g + k * D + d, st[k * D + (((d >> 2) ^ (k & 15)) << 2) + (d & 3)]);
+      }
+    }
   }
 }
 
@@ -236,13 +256,13 @@ struct QCfg {
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = kQBN * D;
-  static constexpr size_t LDS_BYTES = 2 * 2 * TILE * sizeof(u16);
 };
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
   using C = QCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) u16 lds[];
+  // Two K/V buffers, read and filled through __restrict__ pointers (see the dK/dV kernel).
+  __shared__ __attribute__((aligned(16))) u16 kvbuf[4 * C::TILE];
 
   const TileRef tr = map_tile(p, kQBM);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -292,62 +312,68 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
     const int64_t wq_first = qloc0 + 32 * w;
     const bool wave_has_rows = 32 * w < tr.nrows;
 
-    issue_tile<D, kQBN, 4>(Kp, pr.kv_len, lds);
-    issue_tile<D, kQBN, 4>(Vp, pr.kv_len, lds + C::TILE);
-    wait_vmem();
-    __syncthreads();
-
-    for (int kt_ = 0; kt_ < nkt; ++kt_) {
-      const u16* buf = lds + (kt_ & 1) * 2 * C::TILE;
-      const int64_t kbase = (int64_t)kt_ * kQBN;
-      if (kt_ + 1 < nkt) {
-        u16* nb = lds + ((kt_ + 1) & 1) * 2 * C::TILE;
-        issue_tile<D, kQBN, 4>(Kp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nb);
-        issue_tile<D, kQBN, 4>(Vp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nb + C::TILE);
+    auto step = [&](const u16* __restrict__ kb, const u16* __restrict__ vb, u16* __restrict__ nk,
+                    u16* __restrict__ nv, int t) {
+      const int64_t kbase = (int64_t)t * kQBN;
+      if (t + 1 < nkt) {
+        issue_tile<D, kQBN, 4>(Kp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nk);
+        issue_tile<D, kQBN, 4>(Vp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nv);
       }
-
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
       if (active) {
-        const u16* vt = buf + C::TILE;
         f32x16 s[2], dp[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
-          dp[kb] = f32x16{};
+        for (int b = 0; b < 2; ++b) {
+          s[b] = f32x16{};
+          dp[b] = f32x16{};
 #pragma unroll
           for (int kk = 0; kk < C::KK; ++kk) {
-            s[kb] = mfma32(row_operand(buf, kb ? ka1 : ka0, kk), qreg[kk], s[kb]);
-            dp[kb] = mfma32(row_operand(vt, kb ? ka1 : ka0, kk), doreg[kk], dp[kb]);
+            s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
+            dp[b] = mfma32(row_operand(vb, b ? ka1 : ka0, kk), doreg[kk], dp[b]);
           }
         }
+        // Keys past the pair, or after this lane's query in a diagonal pair, are excluded;
+        // kmax is the last visible key of the tile (only edge tiles need it).
         const bool edge = (kbase + kQBN > pr.kv_len) || (diag && kbase + kQBN - 1 > wq_first);
+        int kmax = kQBN - 1;
+        if (edge) {
+          const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
+          kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kQBN - 1 ? kQBN - 1 : lim - kbase));
+        }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, nlse2));
-            if (edge) {
-              const int64_t kj = kbase + kb * 32 + perm_reg_row(r, hh);
-              if (kj >= pr.kv_len || (diag && kj > iq)) pv = 0.f;
-            }
-            dp[kb][r] = (pv * p.scale) * (dp[kb][r] - dl);  // scale * dS^T
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[b][r], p.scale_log2, nlse2));
+            pv = (b * 32 + perm_reg_row(r, hh) > kmax) ? 0.f : pv;
+            dp[b][r] = (pv * p.scale) * (dp[b][r] - dl);  // scale * dS^T
           }
         // B operand dS^T for key step c: registers 8*(c&1) .. +8 of block c>>1.
         bf16x8 dsb[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          bf16x8 t;
+          bf16x8 tt;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) t[e] = (__bf16)dp[c >> 1][8 * (c & 1) + e];
-          dsb[c] = t;
+          for (int e = 0; e < 8; ++e) tt[e] = (__bf16)dp[c >> 1][8 * (c & 1) + e];
+          dsb[c] = tt;
         }
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) dq[db] = mfma32(tr_operand(buf, kt, D, c, db), dsb[c], dq[db]);
+          for (int c = 0; c < 4; ++c) dq[db] = mfma32(tr_operand(kb, kt, D, c, db), dsb[c], dq[db]);
       }
       wait_vmem();
       __syncthreads();
+    };
+
+    issue_tile<D, kQBN, 4>(Kp, pr.kv_len, kvbuf);
+    issue_tile<D, kQBN, 4>(Vp, pr.kv_len, kvbuf + C::TILE);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nkt; ++t) {
+      u16* cur = kvbuf + (t & 1) * 2 * C::TILE;
+      u16* nxt = kvbuf + ((t + 1) & 1) * 2 * C::TILE;
+      step(cur, cur + C::TILE, nxt, nxt + C::TILE, t);
     }
   }
 
@@ -365,32 +391,17 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
   }
 }
 
-template <class K>
-int set_lds(K kernel, size_t bytes, bool* done) {
-  if (*done) return 0;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)bytes);
-  if (e != hipSuccess) return (int)e;
-  *done = true;
-  return 0;
-}
-
 template <int D>
 int launch_bwd(const KParams& kv, const KParams& q, void* stream) {
-  static bool kv_done = false, q_done = false;
   int e;
-  if ((e = set_lds(chunk_bwd_kv_kernel<D>, KvCfg<D>::LDS_BYTES, &kv_done))) return e;
-  if ((e = set_lds(chunk_bwd_q_kernel<D>, QCfg<D>::LDS_BYTES, &q_done))) return e;
   const int64_t nkv = (int64_t)kv.B * kv.Hq * kv.tiles_per_head;
   if (nkv > 0) {
-    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), KvCfg<D>::LDS_BYTES,
-                       (hipStream_t)stream, kv);
+    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   const int64_t nq = (int64_t)q.B * q.Hq * q.tiles_per_head;
   if (nq > 0) {
-    hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), QCfg<D>::LDS_BYTES,
-                       (hipStream_t)stream, q);
+    hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, (hipStream_t)stream, q);
     if ((e = (int)hipGetLastError())) return e;
   }
   return 0;

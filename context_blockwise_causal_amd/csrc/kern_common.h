@@ -111,7 +111,7 @@ __device__ __forceinline__ bf16x8 row_operand(const u16* T, const RowAddr& a, in
 // swizzle of those rows does not depend on c, so one address per (db, half) is precomputed and
 // c enters as an immediate offset.
 struct TrAddr {
-  int lo[4], hi[4];
+  int lo, hi;  // addresses for db = 0; db enters by XOR into element bits 5..6
 };
 
 __device__ __forceinline__ TrAddr make_tr_addr(int lane, int rowlen) {
@@ -120,18 +120,15 @@ __device__ __forceinline__ TrAddr make_tr_addr(int lane, int rowlen) {
   const int r = 8 * (g >> 1) + (j >> 2);
   const int t = 2 * (g & 1) + ((j & 3) >> 1);
   const int within = 4 * (j & 1);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    a.lo[db] = r * rowlen + (((4 * db + t) ^ swz(r, rowlen)) << 3) + within;
-    a.hi[db] = (r + 4) * rowlen + (((4 * db + t) ^ swz(r + 4, rowlen)) << 3) + within;
-  }
+  a.lo = r * rowlen + ((t ^ swz(r, rowlen)) << 3) + within;
+  a.hi = (r + 4) * rowlen + ((t ^ swz(r + 4, rowlen)) << 3) + within;
   return a;
 }
 
 __device__ __forceinline__ bf16x8 tr_operand(const u16* T, const TrAddr& a, int rowlen, int c, int db) {
   const int off = 16 * c * rowlen;
-  const v4i16 lo = ds_read_tr16(T + a.lo[db] + off);
-  const v4i16 hi = ds_read_tr16(T + a.hi[db] + off);
+  const v4i16 lo = ds_read_tr16(T + (a.lo ^ (db << 5)) + off);
+  const v4i16 hi = ds_read_tr16(T + (a.hi ^ (db << 5)) + off);
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, w);

@@ -122,20 +122,23 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
           for (int kk = 0; kk < C::KK; ++kk)
             s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
         }
+        // Keys past the pair, or after this lane's query in a diagonal pair, are excluded; kmax
+        // is the last visible key of the tile (only edge tiles take the masked path).
         const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
+        if (edge) {
+          const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
+          const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kBN - 1 ? kBN - 1 : lim - kbase));
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (b * 32 + perm_reg_row(r, hh) > kmax) s[b][r] = -__builtin_inff();
+        }
         float mx = -__builtin_inff();
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float v = s[b][r];
-            if (edge) {
-              const int64_t kj = kbase + b * 32 + perm_reg_row(r, hh);
-              if (kj >= pr.kv_len || (diag && kj > iq)) v = -__builtin_inff();
-            }
-            s[b][r] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
         // Lazy rescale: the reference m2 moves only when a row's tile max exceeds it by more
         // than kLazyLog2, so exp2(score - m2) <= 2^kLazyLog2 and U, l stay consistent with m2.
