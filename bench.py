@@ -55,205 +55,175 @@ def cpu_baseline(wl, t, target_s: float):
     rank = wl.ranks[0]
     pos = O.rank_positions(wl.seq_len, wl.cp, wl.layout, rank)
     n_rep = wl.heads_q // wl.heads_kv
-    heads = list(range(n_rep))  # the query heads of key/value head 0
-    q = t.as_f64("q")[:1, heads]
-    k = t.as_f64("k")[:1, :1]
-    v = t.as_f64("v")[:1, :1]
-    do = t.as_f64("do")[:1, heads]
     kpos = np.arange(wl.seq_len)
-    # take rows from the end of the slice (the rows with the most visible keys)
+    q_all, k_all, v_all, do_all = (t.as_f64(n)[:1] for n in ("q", "k", "v", "do"))
 
-    def run(nrows):
+    # rows from the end of the slice (the rows with the most visible keys), then more key/value
+    # groups (each with its n_rep query heads) until the sample takes about target_s
+    def run(nrows, ngroups):
         rows = pos[-nrows:]
         t0 = time.perf_counter()
-        O.attention_rows(q[:, :, rows], k, v, rows, kpos)
-        O.attention_rows_bwd(q[:, :, rows], k, v, do[:, :, rows], rows, kpos)
+        for g in range(ngroups):
+            heads = list(range(g * n_rep, (g + 1) * n_rep))
+            q, do = q_all[:, heads][:, :, rows], do_all[:, heads][:, :, rows]
+            k, v = k_all[:, g:g + 1], v_all[:, g:g + 1]
+            O.attention_rows(q, k, v, rows, kpos)
+            O.attention_rows_bwd(q, k, v, do, rows, kpos)
         dt = time.perf_counter() - t0
         vis = float(np.sum(rows + 1))  # keys visible to each row (causal, full sequence)
-        flops = (4 + 10) * wl.head_dim * vis * len(heads)
+        flops = (4 + 10) * wl.head_dim * vis * n_rep * ngroups
         return dt, flops, rows
 
-    n = 16
-    dt, flops, rows = run(n)
+    n, g = 16, 1
+    dt, flops, rows = run(n, g)
     while dt < target_s / 8 and n < len(pos):
         n = min(len(pos), n * 4)
-        dt, flops, rows = run(n)
+        dt, flops, rows = run(n, g)
     if dt < target_s / 2 and n < len(pos):
         n = min(len(pos), int(n * target_s / max(dt, 1e-3) * 0.8))
-        dt, flops, rows = run(n)
+        dt, flops, rows = run(n, g)
+    if dt < target_s / 2 and n == len(pos) and wl.heads_kv > 1:
+        g = min(wl.heads_kv, max(2, int(target_s / max(dt, 1e-3) * 0.8)))
+        dt, flops, rows = run(n, g)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"rank {rank} of {wl.name}: last {len(rows)} rows of the Q slice x {len(heads)} "
-                      f"query heads (one key/value group), forward + backward over the full causal "
+            "sample": f"rank {rank} of {wl.name}: last {len(rows)} rows of the Q slice x {g * n_rep} "
+                      f"query heads ({g} key/value group(s)), forward + backward over the full causal "
                       f"key prefix, FP64, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--same-stream", action="store_true", help="stage K/V on the compute stream")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs a single rank view at a time on one "
-              "MI355X (the ring is simulated on one device); run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    from context_blockwise_causal_amd import api
-    from context_blockwise_causal_amd.inputs import draw
-    from context_blockwise_causal_amd.workloads import WORKLOADS
-    from tests.gpu_util import to_dev
-
-    wl = WORKLOADS[args.workload]
-    prob = api.Problem(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.cp,
-                       wl.layout, wl.dtype)
-    t = draw(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.dtype, wl.seed,
-             with_grad=True)
-    ctx = api.Context(0)
-    dev = {n: to_dev(t.store[n], wl.dtype) for n in ("q", "k", "v", "do")}
-    compute = torch.cuda.current_stream()
-    staging = compute if args.same_stream else torch.cuda.Stream()
-
-    # buffers allocated once, outside the timed region
-    k_ring = torch.empty_like(dev["k"])
-    v_ring = torch.empty_like(dev["v"])
-    bufs = {}
-    for r in wl.ranks:
-        q_sl = torch.empty((wl.batch, wl.heads_q, prob.chunk, wl.head_dim), dtype=prob.torch_dtype,
-                           device="cuda")
-        bufs[r] = dict(q=q_sl, do=torch.empty_like(q_sl), o=torch.empty_like(q_sl),
-                       lse=torch.empty(q_sl.shape[:3], dtype=torch.float32, device="cuda"),
-                       dq=torch.empty_like(q_sl), dk=torch.empty_like(k_ring), dv=torch.empty_like(v_ring))
-    ws_fwd = api.workspace(prob, 0)
-    ws_bwd = api.workspace(prob, 1) if wl.backward else None
-
-    def fwd(r):
-        b = bufs[r]
-        api.ra_rank_view_fwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], ws_fwd,
-                             compute, staging)
-
-    def bwd(r):
-        b = bufs[r]
-        api.ra_rank_view_bwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], b["do"],
-                             b["dq"], b["dk"], b["dv"], ws_bwd, compute, staging)
-
-    def step():
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["k"], k_ring)
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["v"], v_ring)
-        for r in wl.ranks:
-            api.ra_layout_gather(ctx, prob, r, 1, dev["q"], bufs[r]["q"])
-            if wl.backward:
-                api.ra_layout_gather(ctx, prob, r, 1, dev["do"], bufs[r]["do"])
-            fwd(r)
-            if wl.backward:
-                bwd(r)
-
-    def timed(fn, reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record(compute)
-        for _ in range(reps):
-            fn()
-        ev[1].record(compute)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / reps
-
-    fwd_flops = {r: sum(counted_flops(api, prob, r)) for r in wl.ranks}
-    total_fwd = sum(fwd_flops.values())
-    total = total_fwd * (3.5 if wl.backward else 1.0)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    step_ms = timed(step, args.steps)
-
-    # per-pass rates, timed separately (same launches as inside the step)
-    fwd_ms = timed(lambda: [fwd(r) for r in wl.ranks], max(2, args.steps))
-    bwd_ms = timed(lambda: [bwd(r) for r in wl.ranks], max(2, args.steps)) if wl.backward else None
-
-    # dominant kernel: replay the chunk launches of the first rank view with events on the
-    # launch stream, to get the kernel's own average duration.
-    roof = kernel_roofline(api, ctx, prob, wl, dev, k_ring, v_ring, bufs, compute, wl.backward)
-
-    value = total / (step_ms * 1e-3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": "synthetic: seeded N(0,1) Q/K/V/dO, bf16 round-to-nearest-even; model shapes only",
-        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
-                   "heads_q": wl.heads_q, "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
-                   "cp": wl.cp, "layout": wl.layout, "ranks": list(wl.ranks),
-                   "passes": "fwd+bwd" if wl.backward else "fwd"},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd_tflops": round(total_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-        "fwd_frac_of_peak": round(total_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "counted_tflop_per_step": round(total / 1e12, 4),
-    }
-    if wl.backward:
-        bt = total_fwd * 2.5 / (bwd_ms * 1e-3) / 1e12
-        out["bwd_tflops"] = round(bt, 2)
-        out["bwd_frac_of_peak"] = round(bt / PEAK_BF16_TFLOPS, 4)
-    out["roofline"] = roof
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, t, args.cpu_seconds)
-    ctx.close()
-    print(json.dumps(out), flush=True)
-
-
-def kernel_roofline(api, ctx, prob, wl, dev, k_ring, v_ring, bufs, stream, backward):
-    import torch
-    r = wl.ranks[0]
-    b = bufs[r]
+def chunk_launches(api, prob, wl, k_ring, v_ring):
+    """The chunk-kernel launches of every rank view of the workload: (rank, pairs, k, v, fwd FLOPs)."""
     chunk = prob.chunk
-    launches = []
-    for i in range(prob.cp):
-        owner, pairs = api.ra_plan_step(prob, r, i)
-        if all(p[4] == 2 for p in pairs):
-            continue
-        f = counted_flops(api, prob, r)[i] * (2.5 if backward else 1.0)
-        kc = k_ring[:, :, owner * chunk:(owner + 1) * chunk].contiguous()
-        vc = v_ring[:, :, owner * chunk:(owner + 1) * chunk].contiguous()
-        launches.append((pairs, kc, vc, f))
+    out = []
+    for r in wl.ranks:
+        flops = counted_flops(api, prob, r)
+        for i in range(prob.cp):
+            owner, pairs = api.ra_plan_step(prob, r, i)
+            if all(p[4] == 2 for p in pairs):
+                continue
+            kc = k_ring[:, :, owner * chunk:(owner + 1) * chunk].contiguous()
+            vc = v_ring[:, :, owner * chunk:(owner + 1) * chunk].contiguous()
+            out.append((r, pairs, kc, vc, flops[i]))
+    return out
+
+
+# Algorithmic FLOPs of each chunk kernel per unit of counted forward FLOPs: the forward does
+# Q K^T and P V; the dK/dV kernel S, dP, dV and dK; the dQ kernel S, dP and dQ.
+KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_kernel": 2.0, "chunk_bwd_q_kernel": 1.5}
+
+
+def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
+    """One callable per chunk kernel, each launching exactly that kernel for a launch tuple."""
+    import torch
+    chunk = prob.chunk
+    U, m, l = api.new_state(prob, chunk)
+    api.ra_state_init(ctx, prob, U, m, l)
+    run = {"chunk_fwd_bf16_kernel": lambda L: api.ra_chunk_fwd(
+        ctx, prob, bufs[L[0]]["q"], L[2], L[3], L[1], U, m, l, stream)}
     if backward:
-        name = "chunk_bwd_bf16_kernel"
-        delta = api.ra_bwd_preprocess(ctx, prob, b["o"], b["do"])
+        delta = {r: api.ra_bwd_preprocess(ctx, prob, bufs[r]["o"], bufs[r]["do"]) for r in wl.ranks}
         dq = torch.zeros((prob.batch, prob.heads_q, chunk, prob.head_dim), device="cuda")
         dk = torch.zeros((prob.batch, prob.heads_kv, chunk, prob.head_dim), device="cuda")
         dv = torch.zeros_like(dk)
-        run = lambda L: api.ra_chunk_bwd(ctx, prob, b["q"], b["do"], b["lse"], delta, L[1], L[2], L[0],
-                                         dq, dk, dv, stream)
-    else:
-        name = "chunk_fwd_bf16_kernel"
-        U, m, l = api.new_state(prob, chunk)
-        api.ra_state_init(ctx, prob, U, m, l)
-        run = lambda L: api.ra_chunk_fwd(ctx, prob, b["q"], L[1], L[2], L[0], U, m, l, stream)
-    for L in launches:
-        run(L)
-    torch.cuda.synchronize()
-    reps = 3
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
-    times = [0.0] * len(launches)
-    for _ in range(reps):
-        for j, L in enumerate(launches):
-            ev[j][0].record(stream)
-            run(L)
-            ev[j][1].record(stream)
+        b = lambda L: bufs[L[0]]
+        run["chunk_bwd_kv_kernel"] = lambda L: api.ra_chunk_bwd(
+            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], None, dk, dv, stream)
+        run["chunk_bwd_q_kernel"] = lambda L: api.ra_chunk_bwd(
+            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], dq, None, None, stream)
+    return run
+
+
+def kernel_rates(api, ctx, prob, wl, bufs, launches, stream, backward, reps=3):
+    """Average launch duration of each chunk kernel over the workload's launches, timed with
+    HIP events on the launch stream, and its algorithmic rate."""
+    import torch
+    run = kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward)
+    out = {}
+    for name, fn in run.items():
+        for L in launches:
+            fn(L)
         torch.cuda.synchronize()
-        for j in range(len(launches)):
-            times[j] += ev[j][0].elapsed_time(ev[j][1]) / reps
-    flops = sum(L[3] for L in launches)
-    avg_ms = sum(times) / len(launches)
-    achieved = flops / len(launches) / (avg_ms * 1e-3) / 1e12
-    return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "avg_launch_ms": round(avg_ms, 4), "launches_per_rank_view": len(launches),
-            "rank": r, "per_launch_ms": [round(x, 4) for x in times]}
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+        times = [0.0] * len(launches)
+        for _ in range(reps):
+            for j, L in enumerate(launches):
+                ev[j][0].record(stream)
+                fn(L)
+                ev[j][1].record(stream)
+            torch.cuda.synchronize()
+            for j in range(len(launches)):
+                times[j] += ev[j][0].elapsed_time(ev[j][1]) / reps
+        flops = KERNEL_UNITS[name] * sum(L[4] for L in launches) / len(launches)
+        avg_ms = sum(times) / len(launches)
+        out[name] = {"avg_launch_ms": round(avg_ms, 4), "launches": len(launches),
+                     "algorithmic_tflop_per_launch": round(flops / 1e12, 5),
+                     "achieved_tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+                     "frac": round(flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "total_ms_per_pass": round(sum(times), 4)}
+    return out
+
+
+def source_hash():
+    """Hash of the kernel sources: stored counter readings are used only while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "context_blockwise_causal_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(wl_name):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_chunk_kernels_{wl_name}.json")
+
+
+def stored_traffic(wl_name, kernel):
+    """HBM bytes per launch of `kernel` from the stored counter readings, if they were taken
+    on the current kernel sources; else None."""
+    try:
+        rec = json.load(open(traffic_path(wl_name)))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
+
+
+def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes):
+    """Turns two rocprofv3 --pmc runs of `--kernels-only` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into bytes per launch, scaled by what the counters read for the calibration copy
+    (the layout kernel gathering one K tensor: calib_bytes read and calib_bytes written)."""
+    import csv
+    import glob
+    import re
+
+    def per_kernel(root, counter):
+        acc = {}
+        for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                m = re.search(r"(chunk_\w+|layout_kernel)", r["Kernel_Name"])
+                if not m:
+                    continue
+                a = acc.setdefault(m.group(1), {})
+                a[r["Dispatch_Id"]] = a.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"]) * 1024
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    fs, ws = calib_bytes / fetch["layout_kernel"], calib_bytes / write["layout_kernel"]
+    rec = {"workload": wl_name, "source_hash": source_hash(),
+           "calibration": {"kernel": "layout_kernel", "bytes_each_way": calib_bytes,
+                           "fetch_read": fetch["layout_kernel"], "write_read": write["layout_kernel"],
+                           "fetch_scale": fs, "write_scale": ws},
+           "kernels": {k: {"fetch_bytes_per_launch": fetch[k] * fs, "write_bytes_per_launch": write[k] * ws}
+                       for k in fetch if k.startswith("chunk_") and k in write}}
+    with open(traffic_path(wl_name), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 if __name__ == "__main__":

@@ -224,9 +224,12 @@ def ra_chunk_bwd(ctx, prob: Problem, q, dO, lse, delta, k, v, pairs, dq_acc, dk_
     _need(delta, qs, torch.float32, "delta")
     _need(k, ks, prob.torch_dtype, "k")
     _need(v, ks, prob.torch_dtype, "v")
-    _need(dq_acc, qs + (prob.head_dim,), torch.float32, "dq_acc")
-    _need(dk_acc, ks, torch.float32, "dk_acc")
-    _need(dv_acc, ks, torch.float32, "dv_acc")
+    if dq_acc is not None:
+        _need(dq_acc, qs + (prob.head_dim,), torch.float32, "dq_acc")
+    if dk_acc is not None:
+        _need(dk_acc, ks, torch.float32, "dk_acc")
+    if dv_acc is not None:
+        _need(dv_acc, ks, torch.float32, "dv_acc")
     p = prob.c()
     arr = L.pairs_array(pairs)
     L.call("ra_chunk_bwd", ctx.handle, ctypes.byref(p), _ptr(q), _ptr(dO), _ptr(lse), _ptr(delta),

@@ -395,12 +395,12 @@ template <int D>
 int launch_bwd(const KParams& kv, const KParams& q, void* stream) {
   int e;
   const int64_t nkv = (int64_t)kv.B * kv.Hq * kv.tiles_per_head;
-  if (nkv > 0) {
+  if (nkv > 0 && kv.dk) {
     hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   const int64_t nq = (int64_t)q.B * q.Hq * q.tiles_per_head;
-  if (nq > 0) {
+  if (nq > 0 && q.U) {
     hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, (hipStream_t)stream, q);
     if ((e = (int)hipGetLastError())) return e;
   }

@@ -128,9 +128,11 @@ __global__ __launch_bounds__(64) void chunk_bwd_f32_kernel(const KParams p) {
         }
         pj = expf(s * p.scale - lse);
         dsj = pj * (dp - dl);
-        for (int d = 0; d < D; ++d) {
-          atomicAdd(dKp + j * D + d, p.scale * dsj * qs[d]);
-          atomicAdd(dVp + j * D + d, pj * dos[d]);
+        if (p.dk) {
+          for (int d = 0; d < D; ++d) {
+            atomicAdd(dKp + j * D + d, p.scale * dsj * qs[d]);
+            atomicAdd(dVp + j * D + d, pj * dos[d]);
+          }
         }
       }
       const int nk = (int)(key_end - k0 < 64 ? key_end - k0 : 64);
@@ -141,8 +143,10 @@ __global__ __launch_bounds__(64) void chunk_bwd_f32_kernel(const KParams p) {
       }
     }
   }
+  if (p.U) {
 #pragma unroll
-  for (int t = 0; t < PER; ++t) p.U[qrow * D + lane + 64 * t] += p.scale * dq[t];
+    for (int t = 0; t < PER; ++t) p.U[qrow * D + lane + 64 * t] += p.scale * dq[t];
+  }
 }
 
 template <int D>

@@ -317,7 +317,13 @@ ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* prob, const void* q, c
   if (st != RA_OK) return st;
   if (q_rows < 0 || kv_rows < 0) return fail(RA_ERR_INVALID, "row counts must be >= 0");
   if ((st = check_pairs(pairs, n_pairs, q_rows, kv_rows)) != RA_OK) return st;
-  if ((st = need_ptrs({q, dO, lse, delta, k, v, dq_acc, dk_acc, dv_acc})) != RA_OK) return st;
+  if ((st = need_ptrs({q, dO, lse, delta, k, v})) != RA_OK) return st;
+  // dq_acc may be NULL (no dQ), or dk_acc and dv_acc together (no dK, dV); not all three.
+  if ((dk_acc == nullptr) != (dv_acc == nullptr))
+    return fail(RA_ERR_INVALID, "dk_acc and dv_acc must both be given or both be NULL");
+  if (!dq_acc && !dk_acc) return fail(RA_ERR_INVALID, "no gradient requested (dq_acc, dk_acc, dv_acc all NULL)");
+  if (dq_acc && (st = need_ptrs({dq_acc})) != RA_OK) return st;
+  if (dk_acc && (st = need_ptrs({dk_acc, dv_acc})) != RA_OK) return st;
   KParams kp = base_params(s);
   kp.q = q; kp.dO = dO; kp.lse = lse; kp.delta = delta; kp.k = k; kp.v = v;
   kp.U = dq_acc; kp.dk = dk_acc; kp.dv = dv_acc;

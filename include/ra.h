@@ -178,7 +178,10 @@ ra_status ra_bwd_preprocess(ra_context* ctx, const ra_problem* problem, int64_t 
  * q, dO: (batch, heads_q, q_rows, head_dim); lse, delta: (batch, heads_q, q_rows) fp32;
  * k, v: (batch, heads_kv, kv_rows, head_dim); dq_acc like q, dk_acc/dv_acc like k (fp32).
  * dk/dv of a key/value head sum the contributions of all heads_q/heads_kv query heads that
- * read it, inside the kernel.  Accumulation uses fp32 atomics: summation order varies. */
+ * read it, inside the kernel.  Accumulation uses fp32 atomics: summation order varies.
+ * Gradients that are not needed may be left out: dq_acc = NULL computes dK and dV only;
+ * dk_acc = dv_acc = NULL computes dQ only (the bf16 path then runs one kernel instead of two).
+ * RA_ERR_INVALID if only one of dk_acc, dv_acc is NULL or all three are. */
 ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* problem, const void* q, const void* dO,
                        const float* lse, const float* delta, int64_t q_rows, const void* k,
                        const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,

@@ -294,3 +294,34 @@ def test_chunk_bwd_zigzag_local_step_accumulates(ctx, D, Hq, Hkv, dtype):
     f32 = lambda a: np.asarray(a, np.float32).astype(np.float64)
     for got, b, ref, name in ((dq, base[0], rdq, "dQ"), (dk, base[1], rdk, "dK"), (dv, base[2], rdv, "dV")):
         assert_close(to_f64(got) - f32(b), ref, dtype, name)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,dtype", CASES)
+def test_chunk_bwd_partial_gradients(ctx, D, Hq, Hkv, dtype):
+    """dq_acc = NULL gives dK, dV only; dk_acc = dv_acc = NULL gives dQ only; each matches the
+    oracle and leaves the gradient it was not asked for alone."""
+    B, qlen, kvlen = 1, (96 if dtype == "f32" else 190), (96 if dtype == "f32" else 260)
+    prob = api.Problem(B, 2 * max(qlen, kvlen), Hq, Hkv, D, 1, "contiguous", dtype)
+    q = to_dev(rand_store((B, Hq, qlen, D), dtype, 81), dtype)
+    k = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 82), dtype)
+    v = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 83), dtype)
+    do = to_dev(rand_store((B, Hq, qlen, D), dtype, 84), dtype)
+    qp, kp = O.pair_positions(O.FULL, qlen, kvlen)
+    q64, k64, v64, do64 = (to_f64(t) for t in (q, k, v, do))
+    o, lse, delta = oracle_stats(q64, k64, v64, do64, qp, kp)
+    lse_d = torch.tensor(lse, dtype=torch.float32, device="cuda")
+    dl_d = torch.tensor(delta, dtype=torch.float32, device="cuda")
+    pairs = [(0, 0, qlen, kvlen, L.RA_MASK_FULL)]
+    rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, qp, kp)
+    dk = torch.zeros(B, Hkv, kvlen, D, device="cuda")
+    dv = torch.zeros_like(dk)
+    api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, None, dk, dv)
+    dq = torch.zeros(B, Hq, qlen, D, device="cuda")
+    api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq, None, None)
+    torch.cuda.synchronize()
+    for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
+        assert_close(to_f64(got), ref, dtype, name)
+    with pytest.raises(ValueError):
+        api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq, dk, None)
+    with pytest.raises(ValueError):
+        api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, None, None, None)
