@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   float* const exbuf = reinterpret_cast<float*>(lds + kKvBN * D + 4 * C::QT);
 
   const TileRef tr = map_tile(p, kKvBN);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int kl = 32 * w + lq;  // this lane's key within the tile
   const bool kvalid = kl < tr.nrows;
   const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
   __shared__ __attribute__((aligned(16))) u16 kvbuf[4 * C::TILE];
 
   const TileRef tr = map_tile(p, kQBM);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int qi = 32 * w + lq;
   const bool qvalid = qi < tr.nrows;
   const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
@@ -321,17 +321,14 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
       }
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
       if (active) {
-        f32x16 s[2], dp[2];
+        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = f32x16{};
-          dp[b] = f32x16{};
+        for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-          for (int kk = 0; kk < C::KK; ++kk) {
+          for (int b = 0; b < 2; ++b) {
             s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
             dp[b] = mfma32(row_operand(vb, b ? ka1 : ka0, kk), doreg[kk], dp[b]);
           }
-        }
         // Keys past the pair, or after this lane's query in a diagonal pair, are excluded;
         // kmax is the last visible key of the tile (only edge tiles need it).
         const bool edge = (kbase + kQBN > pr.kv_len) || (diag && kbase + kQBN - 1 > wq_first);

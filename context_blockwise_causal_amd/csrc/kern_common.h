@@ -134,6 +134,24 @@ __device__ __forceinline__ bf16x8 tr_operand(const u16* T, const TrAddr& a, int 
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Index of the calling wavefront in its workgroup, as a wave-uniform (scalar) value: derived
+// from threadIdx it would be treated as per-lane, and everything computed from it would take
+// vector registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Sum / max of a value and its partner 32 lanes away, every lane getting the result, without
+// going through LDS: v_permlane32_swap (gfx950) leaves, in each lane, v of lane l and of lane
+// l ^ 32 in its two outputs.
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Direct global -> LDS loads (global_load_lds_dwordx4): every lane copies 16 bytes from its own
 // global address to LDS at dst + 16 * lane, where dst must be wave-uniform.  The data does not
 // pass through VGPRs; completion is counted by vmcnt, so wait_vmem() followed by a barrier makes
@@ -157,15 +175,16 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t va
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
   constexpr int NI = ROWS / RPI;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   static_assert(NI % NWAVES == 0, "tile rows must split evenly over the wavefronts");
+  const int last = (int)(valid_rows < ROWS ? valid_rows : ROWS) - 1;
 #pragma unroll
   for (int k = 0; k < NI / NWAVES; ++k) {
     const int i = k * NWAVES + w;
     const int row = i * RPI + lane / CH;
     const int c = (lane % CH) ^ swz(row, D);
-    const int64_t gr = row < valid_rows ? row : valid_rows - 1;
-    g2lds16(g + gr * D + c * 8, tile + i * 512);
+    const unsigned off = (unsigned)((row < last ? row : last) * D + c * 8) * 2u;  // bytes
+    g2lds16(reinterpret_cast<const char*>(g) + off, tile + i * 512);
   }
 }
 

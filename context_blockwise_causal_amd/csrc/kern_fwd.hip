@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
   __shared__ __attribute__((aligned(16))) u16 k0[C::TILE], v0[C::TILE], k1[C::TILE], v1[C::TILE];
 
   const TileRef tr = map_tile(p, kBM);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int qi = 32 * w + lq;  // this lane's query row within the tile
   const bool qvalid = qi < tr.nrows;
   const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
@@ -114,32 +114,34 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
       // Skip the math when the whole tile lies in the future of every query of this wave.
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
       if (active) {
-        f32x16 s[2];
+        // The two 32-key blocks' accumulation chains are interleaved, so that each MFMA's
+        // operand read has the other chain's MFMA to hide behind.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = f32x16{};
+        for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-          for (int kk = 0; kk < C::KK; ++kk)
-            s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
-        }
+          for (int b = 0; b < 2; ++b) s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
         // Keys past the pair, or after this lane's query in a diagonal pair, are excluded; kmax
         // is the last visible key of the tile (only edge tiles take the masked path).
         const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
         if (edge) {
           const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
           const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kBN - 1 ? kBN - 1 : lim - kbase));
+          // key of register r in block b is 32 b + perm_reg_row(r, 0) + 8 hh: compare the
+          // compile-time part against kmax - 8 hh
+          const int kmh = kmax - 8 * hh;
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (b * 32 + perm_reg_row(r, hh) > kmax) s[b][r] = -__builtin_inff();
+              if (b * 32 + perm_reg_row(r, 0) > kmh) s[b][r] = -__builtin_inff();
         }
         float mx = -__builtin_inff();
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+        mx = xor32_max(mx) * p.scale_log2;
         // Lazy rescale: the reference m2 moves only when a row's tile max exceeds it by more
         // than kLazyLog2, so exp2(score - m2) <= 2^kLazyLog2 and U, l stay consistent with m2.
         const bool grow = mx > m2 + kLazyLog2;
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
             s[b][r] = e;
             rs += e;
           }
-        rs += __shfl_xor(rs, 32);
+        rs = xor32_sum(rs);
         lsum += rs;
 
         // B operand P^T for key step c (16 keys): registers 8*(c&1) .. +8 of block c>>1.
