@@ -15,6 +15,7 @@ RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_DEVICE, RA_ERR_WORKSPACE = ran
 RA_F32, RA_BF16 = 0, 1
 RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
 RA_MASK_FULL, RA_MASK_DIAG, RA_MASK_SKIP = 0, 1, 2
+RA_A2A_SEQ_PACK, RA_A2A_HEAD_UNPACK, RA_A2A_HEAD_PACK, RA_A2A_SEQ_UNPACK = 0, 1, 2, 3
 
 
 class ra_problem(ctypes.Structure):
@@ -57,6 +58,7 @@ SIGNATURES = {
     "ra_create": [_I32, ctypes.POINTER(_P)],
     "ra_layout_gather": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
     "ra_layout_scatter": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
+    "ra_ulysses_reshard": [_P, _PROB, _I32, _I64, _P, _P, _P],
     "ra_state_init": [_P, _PROB, _I64, _FP, _FP, _FP, _P],
     "ra_chunk_fwd": [_P, _PROB, _P, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP, _FP, _P],
     "ra_lse_merge": [_P, _PROB, _I64, _FP, _FP, _FP, _FP, _FP, _P],

@@ -138,6 +138,32 @@ def ra_layout_scatter(ctx, prob: Problem, rank_begin: int, rank_count: int, part
     return full
 
 
+def reshard_shapes(prob: Problem, step: int, heads: int):
+    """(src shape, dst shape) of a Ulysses re-shard step over `heads` heads."""
+    cp, B, S, D = prob.cp, prob.batch, prob.seq_len, prob.head_dim
+    Hh, Sc = heads // cp, S // cp
+    seq, xbuf, head = (B, heads, Sc, D), (cp, B, Hh, Sc, D), (B, Hh, S, D)
+    return {L.RA_A2A_SEQ_PACK: (seq, xbuf), L.RA_A2A_HEAD_UNPACK: (xbuf, head),
+            L.RA_A2A_HEAD_PACK: (head, xbuf), L.RA_A2A_SEQ_UNPACK: (xbuf, seq)}[step]
+
+
+def ra_ulysses_reshard(ctx, prob: Problem, step: int, heads: int, src, dst=None, stream=None):
+    """One Ulysses re-shard step (see include/ra.h); allocates dst when not given."""
+    if heads % prob.cp or prob.seq_len % prob.cp:
+        raise ValueError("heads and seq_len must be divisible by cp")
+    if step not in (L.RA_A2A_SEQ_PACK, L.RA_A2A_HEAD_UNPACK, L.RA_A2A_HEAD_PACK, L.RA_A2A_SEQ_UNPACK):
+        raise ValueError(f"unknown re-shard step {step}")
+    ss, ds = reshard_shapes(prob, step, heads)
+    _need(src, ss, prob.torch_dtype, "src")
+    if dst is None:
+        dst = torch.empty(ds, dtype=prob.torch_dtype, device=src.device)
+    _need(dst, ds, prob.torch_dtype, "dst")
+    p = prob.c()
+    L.call("ra_ulysses_reshard", ctx.handle, ctypes.byref(p), step, heads, _ptr(src), _ptr(dst),
+           _stream(stream))
+    return dst
+
+
 def new_state(prob: Problem, rows: int, device="cuda"):
     U = torch.empty((prob.batch, prob.heads_q, rows, prob.head_dim), dtype=torch.float32, device=device)
     m = torch.empty((prob.batch, prob.heads_q, rows), dtype=torch.float32, device=device)

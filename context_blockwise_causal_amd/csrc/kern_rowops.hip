@@ -40,6 +40,51 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(const u32x4* __restric
   else dst[full_i] = src[part_i];
 }
 
+// ---- Ulysses re-shard ---------------------------------------------------------------------------
+// Rows are indexed by (j, b, h', s): j < cp the shard, h' < Hh = heads / cp, s < Sc = S / cp.
+// Layout 0, a sequence shard (B, heads, Sc): row ((b cp + j) Hh + h') Sc + s, i.e. head j Hh + h'.
+// Layout 1, the all-to-all buffer (cp, B, Hh, Sc): row ((j B + b) Hh + h') Sc + s.
+// Layout 2, a head shard (B, Hh, S): row ((b Hh + h') cp + j) Sc + s, i.e. position j Sc + s.
+// Each thread moves 16 bytes; destination rows are visited in order (coalesced writes).
+__device__ __forceinline__ void split_row(unsigned long long r, int layout, unsigned cp, unsigned B,
+                                          unsigned Hh, unsigned Sc, unsigned* j, unsigned* b,
+                                          unsigned* h, unsigned* s) {
+  *s = (unsigned)(r % Sc);
+  r /= Sc;
+  if (layout == 0) {
+    *h = (unsigned)(r % Hh); r /= Hh;
+    *j = (unsigned)(r % cp); *b = (unsigned)(r / cp);
+  } else if (layout == 1) {
+    *h = (unsigned)(r % Hh); r /= Hh;
+    *b = (unsigned)(r % B); *j = (unsigned)(r / B);
+  } else {
+    *j = (unsigned)(r % cp); r /= cp;
+    *h = (unsigned)(r % Hh); *b = (unsigned)(r / Hh);
+  }
+}
+
+__device__ __forceinline__ unsigned long long join_row(int layout, unsigned cp, unsigned B, unsigned Hh,
+                                                       unsigned Sc, unsigned j, unsigned b, unsigned h,
+                                                       unsigned s) {
+  if (layout == 0) return (((unsigned long long)b * cp + j) * Hh + h) * Sc + s;
+  if (layout == 1) return (((unsigned long long)j * B + b) * Hh + h) * Sc + s;
+  return (((unsigned long long)b * Hh + h) * cp + j) * Sc + s;
+}
+
+__global__ __launch_bounds__(kThreads) void reshard_kernel(const u32x4* __restrict__ src,
+                                                           u32x4* __restrict__ dst, int src_layout,
+                                                           int dst_layout, unsigned cp, unsigned B,
+                                                           unsigned Hh, unsigned Sc, unsigned vec_shift,
+                                                           unsigned long long total) {
+  const unsigned long long i = (unsigned long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const unsigned long long row = i >> vec_shift;
+  const unsigned vec = (unsigned)(i & ((1ull << vec_shift) - 1));
+  unsigned j, b, h, s;
+  split_row(row, dst_layout, cp, B, Hh, Sc, &j, &b, &h, &s);
+  dst[i] = src[(join_row(src_layout, cp, B, Hh, Sc, j, b, h, s) << vec_shift) + vec];
+}
+
 // ---- online-softmax state ---------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void state_init_kernel(f32x4* __restrict__ U, float* __restrict__ m,
                                                               float* __restrict__ l, long long nrows,
@@ -196,6 +241,18 @@ int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_
                      (const u32x4*)src, (u32x4*)dst, s.layout == RA_ZIGZAG ? 1 : 0,
                      (unsigned)s.cp, (unsigned)rank_begin, (unsigned)s.chunk, (unsigned)s.crow,
                      rows_out, (unsigned)log2i(row_vec), (unsigned long long)s.S, gather ? 1 : 0);
+  return (int)hipGetLastError();
+}
+
+int launch_reshard(const Shape& s, int32_t step, int64_t heads, const void* src, void* dst, void* stream) {
+  static const int kSrc[4] = {0, 1, 2, 1}, kDst[4] = {1, 2, 1, 0};
+  const long long row_vec = s.D * s.esize / 16;
+  const long long total = s.B * heads * (s.S / s.cp) * row_vec;
+  if (total == 0) return 0;
+  hipLaunchKernelGGL(reshard_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst, kSrc[step], kDst[step], (unsigned)s.cp,
+                     (unsigned)s.B, (unsigned)(heads / s.cp), (unsigned)(s.S / s.cp),
+                     (unsigned)log2i(row_vec), (unsigned long long)total);
   return (int)hipGetLastError();
 }
 

@@ -244,6 +244,20 @@ ra_status ra_layout_scatter(ra_context* ctx, const ra_problem* prob, int32_t ran
   return dev_err(launch_layout(s, rank_begin, rank_count, heads, in, full, false, stream), "layout scatter");
 }
 
+ra_status ra_ulysses_reshard(ra_context* ctx, const ra_problem* prob, int32_t step, int64_t heads,
+                             const void* src, void* dst, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (step < RA_A2A_SEQ_PACK || step > RA_A2A_SEQ_UNPACK) return fail(RA_ERR_INVALID, "unknown re-shard step %d", step);
+  if (heads != s.Hq && heads != s.Hkv) return fail(RA_ERR_INVALID, "heads must be heads_q or heads_kv");
+  if (heads % s.cp) return fail(RA_ERR_INVALID, "heads (%lld) must be divisible by cp_size (%d)", (long long)heads, s.cp);
+  if ((st = need_ptrs({src, dst})) != RA_OK) return st;
+  if (src == dst) return fail(RA_ERR_INVALID, "re-shard cannot run in place");
+  DeviceGuard g(ctx->device);
+  return dev_err(launch_reshard(s, step, heads, src, dst, stream), "ulysses re-shard");
+}
+
 ra_status ra_state_init(ra_context* ctx, const ra_problem* prob, int64_t rows, float* U, float* m,
                         float* l, void* stream) {
   Shape s;

@@ -105,6 +105,8 @@ constexpr int64_t kF32BwdTileRows = 1;
 int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_t heads,
                   const void* src, void* dst, bool gather, void* stream);
 int launch_state_init(int64_t nrows, int64_t D, float* U, float* m, float* l, void* stream);
+// Ulysses re-shard step (ra_a2a_step) over `heads` heads; cp divides heads and S.
+int launch_reshard(const Shape& s, int32_t step, int64_t heads, const void* src, void* dst, void* stream);
 int launch_lse_merge(int64_t nrows, int64_t D, const float* o_part, const float* lse_part,
                      float* U, float* m, float* l, void* stream);
 int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U, const float* m,

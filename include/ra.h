@@ -134,6 +134,31 @@ ra_status ra_layout_scatter(ra_context* ctx, const ra_problem* problem, int32_t 
                             int32_t rank_count, int64_t heads, const void* in, void* full,
                             void* stream);
 
+/* Ulysses re-shard, the on-GPU half of the all-to-all that turns a sequence shard into a head
+ * shard and back ("上下文并行", section Ulysses: the all-to-all exchanges sequence sharding
+ * for head sharding before attention and reverses it after).  cp = problem->cp_size is the
+ * all-to-all degree; it must divide `heads` (heads_q or heads_kv) and seq_len.  With
+ * Hh = heads / cp and Sc = seq_len / cp, the tensors are (element type problem->dtype):
+ *   sequence shard  (batch, heads, Sc, head_dim)          rank r holds positions r Sc ..
+ *   exchange buffer (cp, batch, Hh, Sc, head_dim)          block j goes to / came from rank j
+ *   head shard      (batch, Hh, seq_len, head_dim)         rank r holds heads r Hh ..
+ * RA_A2A_SEQ_PACK:    sequence shard -> send buffer (block j = this shard's heads of rank j)
+ * RA_A2A_HEAD_UNPACK: receive buffer (block j = rank j's positions) -> head shard
+ * RA_A2A_HEAD_PACK:   head shard -> send buffer (block j = positions of rank j)
+ * RA_A2A_SEQ_UNPACK:  receive buffer (block j = heads of rank j) -> sequence shard
+ * The all-to-all itself (receive block j on rank r = send block r of rank j) is the
+ * collective and not part of this library.  A pure permutation: bit-exact.  src and dst must
+ * not overlap; RA_ERR_INVALID otherwise, for an unknown step, or heads not divisible by cp. */
+typedef enum {
+  RA_A2A_SEQ_PACK = 0,
+  RA_A2A_HEAD_UNPACK = 1,
+  RA_A2A_HEAD_PACK = 2,
+  RA_A2A_SEQ_UNPACK = 3
+} ra_a2a_step;
+
+ra_status ra_ulysses_reshard(ra_context* ctx, const ra_problem* problem, int32_t step,
+                             int64_t heads, const void* src, void* dst, void* stream);
+
 /* Empty online-softmax state for (batch, heads_q, rows): U = 0, m = -inf, l = 0. */
 ra_status ra_state_init(ra_context* ctx, const ra_problem* problem, int64_t rows, float* U,
                         float* m, float* l, void* stream);
