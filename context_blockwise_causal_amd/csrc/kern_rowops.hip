@@ -45,44 +45,31 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(const u32x4* __restric
 // Layout 0, a sequence shard (B, heads, Sc): row ((b cp + j) Hh + h') Sc + s, i.e. head j Hh + h'.
 // Layout 1, the all-to-all buffer (cp, B, Hh, Sc): row ((j B + b) Hh + h') Sc + s.
 // Layout 2, a head shard (B, Hh, S): row ((b Hh + h') cp + j) Sc + s, i.e. position j Sc + s.
-// Each thread moves 16 bytes; destination rows are visited in order (coalesced writes).
-__device__ __forceinline__ void split_row(unsigned long long r, int layout, unsigned cp, unsigned B,
-                                          unsigned Hh, unsigned Sc, unsigned* j, unsigned* b,
-                                          unsigned* h, unsigned* s) {
-  *s = (unsigned)(r % Sc);
-  r /= Sc;
-  if (layout == 0) {
-    *h = (unsigned)(r % Hh); r /= Hh;
-    *j = (unsigned)(r % cp); *b = (unsigned)(r / cp);
-  } else if (layout == 1) {
-    *h = (unsigned)(r % Hh); r /= Hh;
-    *b = (unsigned)(r % B); *j = (unsigned)(r / B);
-  } else {
-    *j = (unsigned)(r % cp); r /= cp;
-    *h = (unsigned)(r % Hh); *b = (unsigned)(r / Hh);
-  }
-}
-
-__device__ __forceinline__ unsigned long long join_row(int layout, unsigned cp, unsigned B, unsigned Hh,
-                                                       unsigned Sc, unsigned j, unsigned b, unsigned h,
-                                                       unsigned s) {
-  if (layout == 0) return (((unsigned long long)b * cp + j) * Hh + h) * Sc + s;
-  if (layout == 1) return (((unsigned long long)j * B + b) * Hh + h) * Sc + s;
-  return (((unsigned long long)b * Hh + h) * cp + j) * Sc + s;
+// In every layout the Sc rows of one (j, b, h') are contiguous, so the re-shard is a copy of
+// B cp Hh blocks of Sc rows: blockIdx.y picks the block (in destination order), x runs over it.
+__device__ __forceinline__ unsigned long long block_row(int layout, unsigned cp, unsigned B, unsigned Hh,
+                                                        unsigned Sc, unsigned j, unsigned b, unsigned h) {
+  unsigned long long r;
+  if (layout == 0) r = ((unsigned long long)b * cp + j) * Hh + h;
+  else if (layout == 1) r = ((unsigned long long)j * B + b) * Hh + h;
+  else r = ((unsigned long long)b * Hh + h) * cp + j;
+  return r * Sc;
 }
 
 __global__ __launch_bounds__(kThreads) void reshard_kernel(const u32x4* __restrict__ src,
                                                            u32x4* __restrict__ dst, int src_layout,
                                                            int dst_layout, unsigned cp, unsigned B,
-                                                           unsigned Hh, unsigned Sc, unsigned vec_shift,
-                                                           unsigned long long total) {
-  const unsigned long long i = (unsigned long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= total) return;
-  const unsigned long long row = i >> vec_shift;
-  const unsigned vec = (unsigned)(i & ((1ull << vec_shift) - 1));
-  unsigned j, b, h, s;
-  split_row(row, dst_layout, cp, B, Hh, Sc, &j, &b, &h, &s);
-  dst[i] = src[(join_row(src_layout, cp, B, Hh, Sc, j, b, h, s) << vec_shift) + vec];
+                                                           unsigned Hh, unsigned Sc, unsigned vec_shift) {
+  // destination block index -> (j, b, h')
+  unsigned y = blockIdx.y, j, b, h;
+  if (dst_layout == 0) { h = y % Hh; y /= Hh; j = y % cp; b = y / cp; }
+  else if (dst_layout == 1) { h = y % Hh; y /= Hh; b = y % B; j = y / B; }
+  else { j = y % cp; y /= cp; h = y % Hh; b = y / Hh; }
+  const unsigned long long so = block_row(src_layout, cp, B, Hh, Sc, j, b, h) << vec_shift;
+  const unsigned long long dO = block_row(dst_layout, cp, B, Hh, Sc, j, b, h) << vec_shift;
+  const unsigned n = Sc << vec_shift;
+  for (unsigned i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
+    dst[dO + i] = src[so + i];
 }
 
 // ---- online-softmax state ---------------------------------------------------------------------
@@ -247,12 +234,16 @@ int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_
 int launch_reshard(const Shape& s, int32_t step, int64_t heads, const void* src, void* dst, void* stream) {
   static const int kSrc[4] = {0, 1, 2, 1}, kDst[4] = {1, 2, 1, 0};
   const long long row_vec = s.D * s.esize / 16;
-  const long long total = s.B * heads * (s.S / s.cp) * row_vec;
-  if (total == 0) return 0;
-  hipLaunchKernelGGL(reshard_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, (hipStream_t)stream,
-                     (const u32x4*)src, (u32x4*)dst, kSrc[step], kDst[step], (unsigned)s.cp,
-                     (unsigned)s.B, (unsigned)(heads / s.cp), (unsigned)(s.S / s.cp),
-                     (unsigned)log2i(row_vec), (unsigned long long)total);
+  const long long Sc = s.S / s.cp, Hh = heads / s.cp;
+  const long long nblk = s.B * s.cp * Hh;
+  const long long per = Sc * row_vec;
+  if (nblk == 0 || per == 0) return 0;
+  long long gx = (per + kThreads - 1) / kThreads;
+  const long long cap = nblk >= 512 ? 4 : 2048 / nblk;  // enough workgroups to fill the chip
+  if (gx > cap) gx = cap < 1 ? 1 : cap;
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)gx, (unsigned)nblk), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst, kSrc[step], kDst[step],
+                     (unsigned)s.cp, (unsigned)s.B, (unsigned)Hh, (unsigned)Sc, (unsigned)log2i(row_vec));
   return (int)hipGetLastError();
 }
 

@@ -254,6 +254,7 @@ ra_status ra_ulysses_reshard(ra_context* ctx, const ra_problem* prob, int32_t st
   if (heads % s.cp) return fail(RA_ERR_INVALID, "heads (%lld) must be divisible by cp_size (%d)", (long long)heads, s.cp);
   if ((st = need_ptrs({src, dst})) != RA_OK) return st;
   if (src == dst) return fail(RA_ERR_INVALID, "re-shard cannot run in place");
+  if (s.B * heads > 65535) return fail(RA_ERR_UNSUPPORTED, "batch * heads above 65535 in one re-shard");
   DeviceGuard g(ctx->device);
   return dev_err(launch_reshard(s, step, heads, src, dst, stream), "ulysses re-shard");
 }
