@@ -342,6 +342,18 @@ def main():
     fwd_ms = timed(lambda: [fwd(r) for r in wl.ranks], max(2, args.steps))
     bwd_ms = timed(lambda: [bwd(r) for r in wl.ranks], max(2, args.steps)) if wl.backward else None
 
+    # all-gather mode with split-KV: the same forward rank views, chunks computed concurrently
+    # into partials and merged on a second stream
+    ws_split = api.workspace(prob, 2)
+    merge_stream = torch.cuda.Stream()
+
+    def fwd_split(r):
+        b = bufs[r]
+        api.rank_view_fwd_split(ctx, prob, r, b["q"], k_ring, v_ring, ws=ws_split, compute=compute,
+                                merge=merge_stream, out=(b["o"], b["lse"]))
+    fwd_split_ms = timed(lambda: [fwd_split(r) for r in wl.ranks], max(2, args.steps))
+    del ws_split
+
     # each chunk kernel on its own: replay the workload's chunk launches with events on the
     # launch stream; the dominant kernel (most time per pass) gives the roofline entry.
     launches = chunk_launches(api, prob, wl, k_ring, v_ring)
@@ -392,6 +404,9 @@ def main():
         "fwd_frac_of_peak": round(total_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "counted_tflop_per_step": round(total / 1e12, 4),
     }
+    out["split_kv_fwd"] = {"ms": round(fwd_split_ms, 4),
+                           "tflops": round(total_fwd / (fwd_split_ms * 1e-3) / 1e12, 2),
+                           "ring_fwd_ms": round(fwd_ms, 4)}
     if wl.backward:
         bt = total_fwd * 2.5 / (bwd_ms * 1e-3) / 1e12
         out["bwd_tflops"] = round(bt, 2)

@@ -68,6 +68,7 @@ SIGNATURES = {
                      _FP, _P],
     "ra_cast_from_f32": [_P, _PROB, _I64, _FP, _P, _P],
     "ra_rank_view_fwd": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],
+    "ra_rank_view_fwd_split": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],
     "ra_rank_view_bwd": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, _P, _P, _P, _P,
                          ctypes.c_size_t, _P, _P],
 }

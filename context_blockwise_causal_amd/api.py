@@ -329,6 +329,26 @@ def rank_view_fwd(ctx, prob: Problem, rank: int, q_slice, k_ring, v_ring, ws=Non
     return o, lse
 
 
+def rank_view_fwd_split(ctx, prob: Problem, rank: int, q_slice, k_all, v_all, ws=None, compute=None,
+                        merge=None, out=None):
+    """All-gather mode with split-KV (see include/ra.h): returns (o, lse)."""
+    B, Hq, C, D = prob.batch, prob.heads_q, prob.chunk, prob.head_dim
+    _need(q_slice, (B, Hq, C, D), prob.torch_dtype, "q_slice")
+    _need(k_all, (B, prob.heads_kv, prob.seq_len, D), prob.torch_dtype, "k_all")
+    _need(v_all, (B, prob.heads_kv, prob.seq_len, D), prob.torch_dtype, "v_all")
+    if out is None:
+        o = torch.empty_like(q_slice)
+        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q_slice.device)
+    else:
+        o, lse = out
+    if ws is None:
+        ws = workspace(prob, 2, q_slice.device)
+    p = prob.c()
+    L.call("ra_rank_view_fwd_split", ctx.handle, ctypes.byref(p), rank, _ptr(q_slice), _ptr(k_all),
+           _ptr(v_all), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(compute), _stream(merge))
+    return o, lse
+
+
 def rank_view_bwd(ctx, prob: Problem, rank: int, q_slice, k_ring, v_ring, o, lse, dO, ws=None,
                   compute=None, staging=None):
     dq = torch.empty_like(q_slice)

@@ -113,6 +113,27 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(const f32x4* __rest
   }
 }
 
+// Partial state (Up, mp, lp) folded into (U, m, l); same row scheme as lse_merge_kernel.
+__global__ __launch_bounds__(kThreads) void state_merge_kernel(const f32x4* __restrict__ Up,
+                                                               const float* __restrict__ mp,
+                                                               const float* __restrict__ lp,
+                                                               f32x4* __restrict__ U, float* __restrict__ m,
+                                                               float* __restrict__ l, long long nrows,
+                                                               int vec_shift) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (nrows << vec_shift)) return;
+  const long long row = i >> vec_shift;
+  const float mo = m[row], mq = mp[row];
+  const float mn = fmaxf(mo, mq);
+  const float a = rescale(mo, mn), b = rescale(mq, mn);
+  U[i] = a * U[i] + b * Up[i];
+  if ((i & ((1ll << vec_shift) - 1)) == ((1ll << vec_shift) - 1)) {
+    m[row] = mn;
+    l[row] = a * l[row] + b * lp[row];
+  }
+}
+
+
 __device__ __forceinline__ u16 f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(u16, (__bf16)f);
 }
@@ -228,6 +249,16 @@ int launch_layout(const Shape& s, int32_t rank_begin, int32_t rank_count, int64_
                      (const u32x4*)src, (u32x4*)dst, s.layout == RA_ZIGZAG ? 1 : 0,
                      (unsigned)s.cp, (unsigned)rank_begin, (unsigned)s.chunk, (unsigned)s.crow,
                      rows_out, (unsigned)log2i(row_vec), (unsigned long long)s.S, gather ? 1 : 0);
+  return (int)hipGetLastError();
+}
+
+int launch_state_merge(int64_t nrows, int64_t D, const float* Up, const float* mp, const float* lp,
+                       float* U, float* m, float* l, void* stream) {
+  const int vs = log2i(D / 4);
+  const long long n = (long long)nrows << vs;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(state_merge_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const f32x4*)Up, mp, lp, (f32x4*)U, m, l, (long long)nrows, vs);
   return (int)hipGetLastError();
 }
 

@@ -15,11 +15,19 @@
 
 #include "ra_internal.h"
 
+// Streams of the split-KV forward: its chunk launches are independent and run on a small pool
+// of the context's own streams (default priority), so that several can occupy the GPU at once.
+constexpr int kPoolStreams = 4;
+constexpr int kMaxSteps = 64;
+
 struct ra_context {
   int device;
   hipEvent_t start;
   hipEvent_t ready[2];
   hipEvent_t freed[2];
+  hipStream_t pool[kPoolStreams];
+  hipEvent_t done[kMaxSteps];  // chunk i of a split-KV forward has finished
+  hipEvent_t fin;              // the split-KV forward's merges and finalize have finished
 };
 
 namespace ra {
@@ -191,9 +199,14 @@ ra_status ra_create(int32_t device, ra_context** out) {
     e = hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->freed[i], hipEventDisableTiming);
   }
+  for (int i = 0; i < kMaxSteps && e == hipSuccess; ++i)
+    e = hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fin, hipEventDisableTiming);
+  for (int i = 0; i < kPoolStreams && e == hipSuccess; ++i)
+    e = hipStreamCreateWithFlags(&c->pool[i], hipStreamNonBlocking);
   if (e != hipSuccess) {
     delete c;
-    return fail(RA_ERR_DEVICE, "event creation failed: %s", hipGetErrorString(e));
+    return fail(RA_ERR_DEVICE, "event or stream creation failed: %s", hipGetErrorString(e));
   }
   *out = c;
   return RA_OK;
@@ -207,6 +220,9 @@ void ra_destroy(ra_context* c) {
     (void)hipEventDestroy(c->ready[i]);
     (void)hipEventDestroy(c->freed[i]);
   }
+  for (int i = 0; i < kMaxSteps; ++i) (void)hipEventDestroy(c->done[i]);
+  (void)hipEventDestroy(c->fin);
+  for (int i = 0; i < kPoolStreams; ++i) (void)hipStreamDestroy(c->pool[i]);
   delete c;
 }
 
@@ -399,6 +415,72 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     return st;
   return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
                  "forward finalize");
+}
+
+ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* prob, int32_t rank,
+                                 const void* q_slice, const void* k_all, const void* v_all,
+                                 void* o_slice, float* lse_slice, void* workspace,
+                                 size_t workspace_bytes, void* compute, void* merge) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if ((st = check_rank(s, rank)) != RA_OK) return st;
+  if (s.cp > kMaxSteps) return fail(RA_ERR_UNSUPPORTED, "cp_size above %d is not supported", kMaxSteps);
+  if ((st = need_ptrs({q_slice, k_all, v_all, o_slice, lse_slice})) != RA_OK) return st;
+  const SplitWs W = split_ws(s);
+  if (!workspace || !aligned16(workspace)) return fail(RA_ERR_INVALID, "workspace is NULL or misaligned");
+  if (workspace_bytes < W.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, W.total);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t cs = (hipStream_t)compute;
+  hipStream_t ms = merge ? (hipStream_t)merge : cs;
+  DeviceGuard g(ctx->device);
+  int e;
+  const int64_t rows = s.B * s.Hq * s.chunk;
+  const int64_t chunk_bytes = s.chunk * s.D * s.esize;
+  float* U = reinterpret_cast<float*>(ws + W.U);
+  float* m = reinterpret_cast<float*>(ws + W.m);
+  float* l = reinterpret_cast<float*>(ws + W.l);
+  // everything starts after the caller's earlier work on the compute stream
+  if ((e = (int)hipEventRecord(ctx->start, cs))) return dev_err(e, "record start");
+  for (int i = 0; i < kPoolStreams; ++i)
+    if ((e = (int)hipStreamWaitEvent(ctx->pool[i], ctx->start, 0))) return dev_err(e, "pool wait start");
+  if (ms != cs && (e = (int)hipStreamWaitEvent(ms, ctx->start, 0))) return dev_err(e, "merge wait start");
+  if ((e = launch_state_init(rows, s.D, U, m, l, ms))) return dev_err(e, "state init");
+  int np = 0;
+  for (int32_t i = 0; i < s.cp; ++i) {
+    int32_t owner, n;
+    ra_pair pairs[4];
+    plan_step(s, rank, i, &owner, pairs, &n);
+    if (!any_compute(pairs, n)) continue;
+    // partial state of this chunk, computed on a pool stream straight from the gathered K/V
+    char* part = ws + W.part + (size_t)np * W.part_stride;
+    float* Up = reinterpret_cast<float*>(part);
+    float* mp = reinterpret_cast<float*>(part + W.m);
+    float* lp = reinterpret_cast<float*>(part + W.l);
+    hipStream_t ps = ctx->pool[np % kPoolStreams];
+    if ((e = launch_state_init(rows, s.D, Up, mp, lp, ps))) return dev_err(e, "partial state init");
+    KParams kp = base_params(s);
+    kp.q = q_slice; kp.U = Up; kp.m = mp; kp.l = lp;
+    kp.q_head_rows = s.chunk;
+    kp.k = (const char*)k_all + owner * chunk_bytes;
+    kp.v = (const char*)v_all + owner * chunk_bytes;
+    kp.kv_head_rows = s.S;
+    kp.dkv_head_rows = s.S;
+    if ((e = run_fwd(s, kp, pairs, n, ps))) return dev_err(e, "chunk kernel (split)");
+    if ((e = (int)hipEventRecord(ctx->done[np], ps))) return dev_err(e, "record chunk done");
+    // its merge into the running state, on the merge stream, in step order
+    if ((e = (int)hipStreamWaitEvent(ms, ctx->done[np], 0))) return dev_err(e, "merge wait chunk");
+    if ((e = launch_state_merge(rows, s.D, Up, mp, lp, U, m, l, ms))) return dev_err(e, "state merge");
+    ++np;
+  }
+  if ((e = launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, ms)))
+    return dev_err(e, "forward finalize");
+  if (ms != cs) {
+    if ((e = (int)hipEventRecord(ctx->fin, ms))) return dev_err(e, "record fin");
+    if ((e = (int)hipStreamWaitEvent(cs, ctx->fin, 0))) return dev_err(e, "compute wait fin");
+  }
+  return RA_OK;
 }
 
 ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank,

@@ -43,6 +43,9 @@ int64_t slice_chunk(const Shape& s, int32_t rank, int32_t which);
 struct FwdWs { size_t U, m, l, slot[2], total; };
 struct BwdWs { size_t dq, dk, dv, delta, slot[2], total; };
 FwdWs fwd_ws(const Shape& s);
+// Split-KV forward: the running state, then one partial state per ring step (cp of them).
+struct SplitWs { size_t U, m, l, part, part_stride, total; };
+SplitWs split_ws(const Shape& s);
 BwdWs bwd_ws(const Shape& s);
 
 // ---- kernel parameter blocks -------------------------------------------------------------
@@ -109,6 +112,10 @@ int launch_state_init(int64_t nrows, int64_t D, float* U, float* m, float* l, vo
 int launch_reshard(const Shape& s, int32_t step, int64_t heads, const void* src, void* dst, void* stream);
 int launch_lse_merge(int64_t nrows, int64_t D, const float* o_part, const float* lse_part,
                      float* U, float* m, float* l, void* stream);
+// Folds an unnormalised partial state (Up, mp, lp) into (U, m, l): the merge of the normalised
+// partial (Up / lp, mp + ln lp) written without the division.
+int launch_state_merge(int64_t nrows, int64_t D, const float* Up, const float* mp, const float* lp,
+                       float* U, float* m, float* l, void* stream);
 int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U, const float* m,
                         const float* l, void* o, float* lse, void* stream);
 int launch_bwd_preprocess(int64_t nrows, int64_t D, int32_t dtype, const void* o,

@@ -168,6 +168,19 @@ FwdWs fwd_ws(const Shape& s) {
   return w;
 }
 
+SplitWs split_ws(const Shape& s) {
+  SplitWs w;
+  const size_t rows = (size_t)(s.B * s.Hq * s.chunk);
+  const size_t state = align256(rows * s.D * 4) + 2 * align256(rows * 4);
+  w.U = 0;
+  w.m = align256(rows * s.D * 4);
+  w.l = w.m + align256(rows * 4);
+  w.part = state;
+  w.part_stride = state;
+  w.total = state * (size_t)(1 + s.cp);
+  return w;
+}
+
 BwdWs bwd_ws(const Shape& s) {
   BwdWs w;
   const size_t rows = (size_t)(s.B * s.Hq * s.chunk);
@@ -287,7 +300,8 @@ ra_status ra_workspace_size(const ra_problem* problem, int32_t pass, size_t* byt
   if (!bytes) return ra::fail(RA_ERR_INVALID, "bytes is NULL");
   if (pass == 0) *bytes = ra::fwd_ws(s).total;
   else if (pass == 1) *bytes = ra::bwd_ws(s).total;
-  else return ra::fail(RA_ERR_INVALID, "pass must be 0 (forward) or 1 (backward)");
+  else if (pass == 2) *bytes = ra::split_ws(s).total;
+  else return ra::fail(RA_ERR_INVALID, "pass must be 0 (forward), 1 (backward) or 2 (split-KV forward)");
   return RA_OK;
 }
 

@@ -108,7 +108,8 @@ ra_status ra_validate(const ra_problem* problem, int32_t rank);
 ra_status ra_plan_step(const ra_problem* problem, int32_t rank, int32_t step, int32_t* owner,
                        ra_pair pairs[4], int32_t* n_pairs);
 
-/* Workspace bytes needed by ra_rank_view_fwd (pass = 0) or ra_rank_view_bwd (pass = 1). */
+/* Workspace bytes needed by ra_rank_view_fwd (pass = 0), ra_rank_view_bwd (pass = 1) or
+ * ra_rank_view_fwd_split (pass = 2). */
 ra_status ra_workspace_size(const ra_problem* problem, int32_t pass, size_t* bytes);
 
 /* ---- context ----------------------------------------------------------------------- */
@@ -230,6 +231,22 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* problem, int32_t r
                            const void* q_slice, const void* k_ring, const void* v_ring,
                            void* o_slice, float* lse_slice, void* workspace,
                            size_t workspace_bytes, void* compute, void* staging);
+
+/* All-gather mode with split-KV ("上下文并行", 基本思想: the all_gather variant gathers every
+ * K/V chunk and computes with the local Q; Megatron's separate stream that updates the
+ * softmax_lse, "Zig-Zag Ring Attention").  k_all / v_all hold the gathered K/V in the same
+ * owner-major order as k_ring / v_ring.  Every chunk the rank's queries see is computed
+ * independently into its own partial online-softmax state, the chunk launches spread over the
+ * context's own streams so that they can run concurrently; each partial is then merged into
+ * the running state on the `merge` stream (in step order) and the result finalised there, as
+ * in ra_rank_view_fwd.  Outputs equal ra_rank_view_fwd's up to summation order.  Workspace:
+ * ra_workspace_size(problem, 2, ...) bytes (the running state and one partial state per
+ * step).  `merge` may be NULL (merges on the compute stream).  The call returns once all work
+ * is enqueued; `compute` is ordered after all of it.  RA_ERR_UNSUPPORTED for cp_size > 64. */
+ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* problem, int32_t rank,
+                                 const void* q_slice, const void* k_all, const void* v_all,
+                                 void* o_slice, float* lse_slice, void* workspace,
+                                 size_t workspace_bytes, void* compute, void* merge);
 
 /* Rank-view backward.  Inputs as for the forward plus o_slice / lse_slice from it and
  * dO_slice (like q_slice).  Outputs dq_slice (like q_slice) and dk_ring, dv_ring

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES) | set(L.OTHER)
@@ -52,6 +52,7 @@ def test_workspace_sizes():
     assert api.ra_workspace_size(p, 0) == rows * 64 * 4 + 2 * rows * 4 + 2 * slot
     kvel = 2 * 4 * 4096 * 64
     assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot
+    assert api.ra_workspace_size(p, 2) == (1 + 4) * (rows * 64 * 4 + 2 * rows * 4)  # running + 4 partials
     one = api.Problem(1, 512, 2, 2, 128, 1, "contiguous", "f32")
     assert api.ra_workspace_size(one, 0) == 2 * 512 * 128 * 4 + 2 * 4096  # no staging slots at cp=1
 
