@@ -153,8 +153,29 @@ def _key_limit(k_pos: np.ndarray, k_sorted: bool, qmax: int) -> int:
     return len(k_pos)
 
 
-def attention_rows(q, k, v, q_pos, k_pos, scale=None):
-    """Causal attention for the query rows ``q_pos`` against keys at ``k_pos``.
+def visible(q_pos, k_pos, window: int = 0, attn_chunk: int = 0):
+    """Visibility matrix (len(q_pos), len(k_pos)) of the causal mask and its two restrictions.
+
+    Causal: key j is visible to query t iff j <= t ("Zig-Zag Ring Attention": token i sees
+    [1, i]).  The transformers context-parallel page names two further masks the attention
+    call must rebuild over the whole sequence, sliding-window and chunked attention; read as
+    the usual definitions: with a window W > 0 the query also needs t - j < W (itself and the
+    W - 1 keys before it), with an attention chunk C > 0 it needs j // C == t // C (keys of its
+    own chunk of C positions).  0 disables either restriction.
+    """
+    q_pos = np.asarray(q_pos, np.int64)[:, None]
+    k_pos = np.asarray(k_pos, np.int64)[None, :]
+    vis = k_pos <= q_pos
+    if window:
+        vis = vis & (q_pos - k_pos < window)
+    if attn_chunk:
+        vis = vis & (k_pos // attn_chunk == q_pos // attn_chunk)
+    return vis
+
+
+def attention_rows(q, k, v, q_pos, k_pos, scale=None, window: int = 0, attn_chunk: int = 0):
+    """Causal attention for the query rows ``q_pos`` against keys at ``k_pos``, optionally with
+    a sliding window or attention chunks (``visible``).
 
     q: (B, Hq, T, D); k, v: (B, Hkv, Tk, D); float64.  Returns O (B, Hq, T, D) and the
     natural-log LSE (B, Hq, T).  Rows with no visible key get O = 0 and LSE = -inf.
@@ -184,7 +205,7 @@ def attention_rows(q, k, v, q_pos, k_pos, scale=None):
                 if kn == 0:
                     continue
                 s = sc * (q[b, h, r0:r0 + rb] @ k[b, g, :kn].T)
-                vis = k_pos[None, :kn] <= qp[:, None]
+                vis = visible(qp, k_pos[:kn], window, attn_chunk)
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)
                 has = np.isfinite(m)
@@ -197,7 +218,7 @@ def attention_rows(q, k, v, q_pos, k_pos, scale=None):
     return o, lse
 
 
-def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None):
+def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None, window: int = 0, attn_chunk: int = 0):
     """Analytic gradient of sum over the given rows of <dO_t, O_t>.
 
     Returns dq (B, Hq, T, D) and dk, dv (B, Hkv, Tk, D); dk/dv of a key/value head sum the
@@ -216,7 +237,7 @@ def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None):
     Hkv = k.shape[1]
     n_rep = Hq // Hkv
     sc = _scale(D, scale)
-    o, lse = attention_rows(q, k, v, q_pos, k_pos, scale)
+    o, lse = attention_rows(q, k, v, q_pos, k_pos, scale, window, attn_chunk)
     delta = np.sum(do * o, axis=-1)
     k_sorted = bool(np.all(np.diff(k_pos) >= 0))
     dq = np.zeros_like(q)
@@ -234,7 +255,7 @@ def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None):
                 qb = q[b, h, r0:r0 + rb]
                 dob = do[b, h, r0:r0 + rb]
                 s = sc * (qb @ k[b, g, :kn].T)
-                vis = k_pos[None, :kn] <= qp[:, None]
+                vis = visible(qp, k_pos[:kn], window, attn_chunk)
                 lb = lse[b, h, r0:r0 + rb]
                 lb_safe = np.where(np.isfinite(lb), lb, 0.0)
                 p = np.where(vis, np.exp(s - lb_safe[:, None]), 0.0)
@@ -249,7 +270,8 @@ def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None):
 # ----------------------------------------------------------------------------- rank views
 
 
-def rank_view_fwd(q, k, v, cp: int, layout: str, rank: int, scale=None):
+def rank_view_fwd(q, k, v, cp: int, layout: str, rank: int, scale=None, window: int = 0,
+                  attn_chunk: int = 0):
     """O and LSE of one rank's Q slice, from full-sequence Q (B,Hq,S,D), K, V (B,Hkv,S,D).
 
     Rows are independent, so this is the full-sequence causal attention restricted to the
@@ -257,10 +279,11 @@ def rank_view_fwd(q, k, v, cp: int, layout: str, rank: int, scale=None):
     """
     S = q.shape[2]
     pos = rank_positions(S, cp, layout, rank)
-    return attention_rows(np.asarray(q)[:, :, pos], k, v, pos, np.arange(S), scale)
+    return attention_rows(np.asarray(q)[:, :, pos], k, v, pos, np.arange(S), scale, window, attn_chunk)
 
 
-def rank_view_bwd(q, k, v, do_slice, cp: int, layout: str, rank: int, scale=None):
+def rank_view_bwd(q, k, v, do_slice, cp: int, layout: str, rank: int, scale=None, window: int = 0,
+                  attn_chunk: int = 0):
     """dQ of the rank's slice and the rank's full-sequence dK, dV contributions.
 
     ``do_slice`` is dO for the rank's rows (B, Hq, S/cp, D) in slice order.  dK and dV are
@@ -269,7 +292,8 @@ def rank_view_bwd(q, k, v, do_slice, cp: int, layout: str, rank: int, scale=None
     """
     S = q.shape[2]
     pos = rank_positions(S, cp, layout, rank)
-    return attention_rows_bwd(np.asarray(q)[:, :, pos], k, v, do_slice, pos, np.arange(S), scale)
+    return attention_rows_bwd(np.asarray(q)[:, :, pos], k, v, do_slice, pos, np.arange(S), scale,
+                              window, attn_chunk)
 
 
 def ring_order(seq_len: int, cp: int, layout: str) -> np.ndarray:
