@@ -22,13 +22,15 @@ class ra_problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("heads_q", ctypes.c_int64), ("heads_kv", ctypes.c_int64),
                 ("head_dim", ctypes.c_int64), ("cp_size", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("layout", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("window", ctypes.c_int64), ("attn_chunk", ctypes.c_int64)]
 
 
 class ra_pair(ctypes.Structure):
     _fields_ = [("q_row0", ctypes.c_int64), ("kv_row0", ctypes.c_int64),
                 ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
-                ("mask", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("mask", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_pos0", ctypes.c_int64), ("kv_pos0", ctypes.c_int64)]
 
 
 class RAError(RuntimeError):
@@ -125,15 +127,20 @@ def call(func: str, *args):
     check(func, getattr(load(), func)(*args))
 
 
-def problem(batch, seq_len, heads_q, heads_kv, head_dim, cp_size, layout, dtype, scale=0.0):
+def problem(batch, seq_len, heads_q, heads_kv, head_dim, cp_size, layout, dtype, scale=0.0, window=0,
+            attn_chunk=0):
     lay = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG}.get(layout, layout)
     dt = {"f32": RA_F32, "bf16": RA_BF16}.get(dtype, dtype)
-    return ra_problem(batch, seq_len, heads_q, heads_kv, head_dim, cp_size, lay, dt, scale)
+    return ra_problem(batch, seq_len, heads_q, heads_kv, head_dim, cp_size, lay, dt, scale, window,
+                      attn_chunk)
 
 
 def pairs_array(pairs):
-    """[(q_row0, kv_row0, q_len, kv_len, mask), ...] -> ctypes array of ra_pair."""
+    """[(q_row0, kv_row0, q_len, kv_len, mask[, q_pos0, kv_pos0]), ...] -> ctypes array of
+    ra_pair (positions default to 0; they matter only for window / attention-chunk masks)."""
     arr = (ra_pair * max(1, len(pairs)))()
-    for i, (q0, k0, ql, kl, mask) in enumerate(pairs):
-        arr[i] = ra_pair(q0, k0, ql, kl, mask, 0)
+    for i, p in enumerate(pairs):
+        q0, k0, ql, kl, mask = p[:5]
+        qp, kp = (p[5], p[6]) if len(p) > 5 else (0, 0)
+        arr[i] = ra_pair(q0, k0, ql, kl, mask, 0, qp, kp)
     return arr

@@ -29,6 +29,8 @@ class Problem:
     layout: str = "contiguous"
     dtype: str = "bf16"
     scale: float = 0.0
+    window: int = 0       # sliding window (0 = off)
+    attn_chunk: int = 0   # attention chunk (0 = off)
 
     @property
     def chunk(self) -> int:
@@ -40,7 +42,7 @@ class Problem:
 
     def c(self):
         return L.problem(self.batch, self.seq_len, self.heads_q, self.heads_kv, self.head_dim,
-                         self.cp, self.layout, self.dtype, self.scale)
+                         self.cp, self.layout, self.dtype, self.scale, self.window, self.attn_chunk)
 
 
 def _ptr(t):
@@ -95,12 +97,17 @@ def ra_validate(prob: Problem, rank: int = 0):
     L.call("ra_validate", ctypes.byref(p), rank)
 
 
-def ra_plan_step(prob: Problem, rank: int, step: int):
+def ra_plan_step(prob: Problem, rank: int, step: int, positions: bool = False):
+    """(owner, pairs): pairs as (q_row0, kv_row0, q_len, kv_len, mask), plus (q_pos0, kv_pos0)
+    when positions=True."""
     p = prob.c()
     owner = ctypes.c_int32()
     n = ctypes.c_int32()
     arr = (L.ra_pair * 4)()
     L.call("ra_plan_step", ctypes.byref(p), rank, step, ctypes.byref(owner), arr, ctypes.byref(n))
+    if positions:
+        return owner.value, [(a.q_row0, a.kv_row0, a.q_len, a.kv_len, a.mask, a.q_pos0, a.kv_pos0)
+                             for a in arr[:n.value]]
     return owner.value, [(a.q_row0, a.kv_row0, a.q_len, a.kv_len, a.mask) for a in arr[:n.value]]
 
 

@@ -118,7 +118,20 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const int64_t kloc0 = tr.row0 - pr.kv_row0;  // pair-local index of the tile's first key
     const int64_t kj = kloc0 + kl;              // pair-local index of this lane's key
     const int64_t q_begin = diag ? (kloc0 / kKvBQ) * kKvBQ : 0;
-    const int niter = (int)((pr.q_len - q_begin + kKvBQ - 1) / kKvBQ);
+    // Window / attention-chunk restriction: pair-local index of the highest query that sees
+    // this lane's key (non-decreasing in the key), over the wavefront, and the last query step.
+    const bool has_hi = p.window > 0 || p.attn_chunk > 0;
+    int64_t wave_hi_min = 0, wave_hi_max = 0, q_end = pr.q_len;
+    int hi32 = 1 << 30;  // this lane's highest visible query, clamped to [-1, q_len]
+    if (has_hi) {
+      const int64_t hi = highest_query(pr.kv_pos0 + kj, p.window, p.attn_chunk) - pr.q_pos0;
+      hi32 = (int)(hi < -1 ? -1 : (hi > pr.q_len ? pr.q_len : hi));
+      wave_hi_min = highest_query(pr.kv_pos0 + kloc0 + 32 * w, p.window, p.attn_chunk) - pr.q_pos0;
+      wave_hi_max = highest_query(pr.kv_pos0 + kloc0 + 32 * w + 31, p.window, p.attn_chunk) - pr.q_pos0;
+      const int64_t wg_hi = highest_query(pr.kv_pos0 + kloc0 + tr.nrows - 1, p.window, p.attn_chunk) - pr.q_pos0;
+      if (wg_hi + 1 < q_end) q_end = wg_hi + 1;
+    }
+    const int niter = (int)((q_end - q_begin + kKvBQ - 1) / kKvBQ);
     if (niter <= 0) continue;
     const u16* Qp = reinterpret_cast<const u16*>(p.q) + (qhead + pr.q_row0) * D;
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         extra = kv_load_extra(lsep, dltp, qbase + kKvBQ, pr.q_len);
       }
       // The whole wavefront lies in the future of every query of this step (diagonal pairs).
-      const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1);
+      const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1) && !(has_hi && qbase > wave_hi_max);
       if (active) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -147,8 +160,14 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         }
         // Excluded (key, query) pairs: keys past the range, and keys after the query in a
         // diagonal pair.  Only steps on an edge take the masked path.
-        const bool edge = !kvalid || (diag && kloc0 + 32 * w + 31 > qbase);
-        const int qmin = edge ? (kvalid ? (int)(kj - qbase) : 1 << 20) : -1;  // first visible query
+        const bool edge = !kvalid || (diag && kloc0 + 32 * w + 31 > qbase) ||
+                          (has_hi && qbase + kKvBQ - 1 > wave_hi_min);
+        // first and last visible query of this lane's key in the step
+        const int qmin = !edge ? -1 : (!kvalid ? 1 << 20 : (diag ? (int)(kj - qbase) : -1));
+        const int qmax = edge ? hi32 - (int)qbase : 1 << 20;  // last visible query of the step
+        // query of register 4j+i is perm_reg_row(4j+i, 0) + 8 hh: compare the compile-time part
+        // against the bounds shifted by 8 hh
+        const int qml = qmin - 8 * hh, qmh = qmax - 8 * hh;
         const float* lse2s = ex;
         const float* dlts = ex + kKvBQ;
 #pragma unroll
@@ -160,10 +179,19 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * j + i;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -l4[i]));
-            pv = (r0 + i < qmin) ? 0.f : pv;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -l4[i]));
             s[r] = pv;
             dp[r] = (pv * p.scale) * (dp[r] - d4[i]);  // scale * dS
+          }
+        }
+        if (edge) {  // excluded (key, query) pairs get P = dS = 0
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qr = perm_reg_row(r, 0);
+            if (qr < qml || qr > qmh) {
+              s[r] = 0.f;
+              dp[r] = 0.f;
+            }
           }
         }
         bf16x8 pb[2], dsb[2];
@@ -311,6 +339,17 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
     const u16* Vp = Vg + (kvhead + pr.kv_row0) * D;
     const int64_t wq_first = qloc0 + 32 * w;
     const bool wave_has_rows = 32 * w < tr.nrows;
+    // Window / attention-chunk restriction: pair-local index of the lowest key this lane's
+    // query sees (non-decreasing in the query), over the wavefront, and the first key tile.
+    const bool has_lo = p.window > 0 || p.attn_chunk > 0;
+    int64_t lo = 0, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
+    if (has_lo) {
+      lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo = lowest_key(pr.q_pos0 + wq_first, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 31, p.window, p.attn_chunk) - pr.kv_pos0;
+      const int64_t tile_lo = lowest_key(pr.q_pos0 + qloc0, p.window, p.attn_chunk) - pr.kv_pos0;
+      kt0 = tile_lo > 0 ? tile_lo / kQBN : 0;
+    }
 
     auto step = [&](const u16* __restrict__ kb, const u16* __restrict__ vb, u16* __restrict__ nk,
                     u16* __restrict__ nv, int t) {
@@ -319,7 +358,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
         issue_tile<D, kQBN, 4>(Kp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nk);
         issue_tile<D, kQBN, 4>(Vp + (kbase + kQBN) * D, pr.kv_len - kbase - kQBN, nv);
       }
-      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
+                          !(has_lo && kbase + kQBN - 1 < wave_lo);
       if (active) {
         f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -331,20 +371,33 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
           }
         // Keys past the pair, or after this lane's query in a diagonal pair, are excluded;
         // kmax is the last visible key of the tile (only edge tiles need it).
-        const bool edge = (kbase + kQBN > pr.kv_len) || (diag && kbase + kQBN - 1 > wq_first);
-        int kmax = kQBN - 1;
+        const bool edge = (kbase + kQBN > pr.kv_len) || (diag && kbase + kQBN - 1 > wq_first) ||
+                          (has_lo && kbase < wave_lo_max);
+        int kmax = kQBN - 1, kmin = 0;
         if (edge) {
           const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
           kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kQBN - 1 ? kQBN - 1 : lim - kbase));
+          if (has_lo) kmin = (int)(lo - kbase < 0 ? 0 : (lo - kbase > kQBN ? kQBN : lo - kbase));
         }
+        // key of register r in block b is 32 b + perm_reg_row(r, 0) + 8 hh: compare the
+        // compile-time part against the bounds shifted by 8 hh
+        const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[b][r], p.scale_log2, nlse2));
-            pv = (b * 32 + perm_reg_row(r, hh) > kmax) ? 0.f : pv;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[b][r], p.scale_log2, nlse2));
             dp[b][r] = (pv * p.scale) * (dp[b][r] - dl);  // scale * dS^T
           }
+        if (edge) {  // excluded keys get dS = 0
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = b * 32 + perm_reg_row(r, 0);
+              if (key > kmh || key < kml) dp[b][r] = 0.f;
+            }
+        }
         // B operand dS^T for key step c: registers 8*(c&1) .. +8 of block c>>1.
         bf16x8 dsb[4];
 #pragma unroll
@@ -363,13 +416,14 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
       __syncthreads();
     };
 
-    issue_tile<D, kQBN, 4>(Kp, pr.kv_len, kvbuf);
-    issue_tile<D, kQBN, 4>(Vp, pr.kv_len, kvbuf + C::TILE);
+    if (kt0 >= nkt) continue;  // uniform over the workgroup
+    issue_tile<D, kQBN, 4>(Kp + kt0 * kQBN * D, pr.kv_len - kt0 * kQBN, kvbuf);
+    issue_tile<D, kQBN, 4>(Vp + kt0 * kQBN * D, pr.kv_len - kt0 * kQBN, kvbuf + C::TILE);
     wait_vmem();
     __syncthreads();
-    for (int t = 0; t < nkt; ++t) {
-      u16* cur = kvbuf + (t & 1) * 2 * C::TILE;
-      u16* nxt = kvbuf + ((t + 1) & 1) * 2 * C::TILE;
+    for (int t = (int)kt0; t < nkt; ++t) {
+      u16* cur = kvbuf + ((t - (int)kt0) & 1) * 2 * C::TILE;
+      u16* nxt = kvbuf + ((t - (int)kt0 + 1) & 1) * 2 * C::TILE;
       step(cur, cur + C::TILE, nxt, nxt + C::TILE, t);
     }
   }

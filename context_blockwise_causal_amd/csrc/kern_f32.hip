@@ -49,7 +49,13 @@ __global__ __launch_bounds__(64) void chunk_fwd_f32_kernel(const KParams p) {
     if (pr.mask == RA_MASK_DIAG && iq + 1 < key_end) key_end = iq + 1;
     const float* Kp = K + pr.kv_row0 * D;
     const float* Vp = V + pr.kv_row0 * D;
-    for (int64_t k0 = 0; k0 < key_end; k0 += 64) {
+    // window / attention chunk: the row's lowest visible key (pair-local)
+    int64_t key_begin = 0;
+    if (p.window > 0 || p.attn_chunk > 0) {
+      const int64_t lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      key_begin = lo > 0 ? lo : 0;
+    }
+    for (int64_t k0 = key_begin; k0 < key_end; k0 += 64) {
       const int64_t j = k0 + lane;
       float s = -__builtin_inff();
       if (j < key_end) {
@@ -117,7 +123,12 @@ __global__ __launch_bounds__(64) void chunk_bwd_f32_kernel(const KParams p) {
     const float* Vp = V + pr.kv_row0 * D;
     float* dKp = p.dk + (dkvhead + pr.kv_row0) * D;
     float* dVp = p.dv + (dkvhead + pr.kv_row0) * D;
-    for (int64_t k0 = 0; k0 < key_end; k0 += 64) {
+    int64_t key_begin = 0;
+    if (p.window > 0 || p.attn_chunk > 0) {
+      const int64_t lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      key_begin = lo > 0 ? lo : 0;
+    }
+    for (int64_t k0 = key_begin; k0 < key_end; k0 += 64) {
       const int64_t j = k0 + lane;
       float pj = 0.f, dsj = 0.f;
       if (j < key_end) {

@@ -103,6 +103,17 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
     const u16* Vp = Vg + (kvhead + pr.kv_row0) * D;
     const int64_t wq_first = qloc0 + 32 * w;  // pair-local index of the wavefront's first query
     const bool wave_has_rows = 32 * w < tr.nrows;
+    // Window / attention-chunk restriction: pair-local index of the lowest key this lane's
+    // query sees (non-decreasing in the query), and its range over the wavefront and the tile.
+    const bool has_lo = p.window > 0 || p.attn_chunk > 0;
+    int64_t lo = 0, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
+    if (has_lo) {
+      lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo = lowest_key(pr.q_pos0 + wq_first, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 31, p.window, p.attn_chunk) - pr.kv_pos0;
+      const int64_t tile_lo = lowest_key(pr.q_pos0 + qloc0, p.window, p.attn_chunk) - pr.kv_pos0;
+      kt0 = tile_lo > 0 ? tile_lo / kBN : 0;  // key tiles below every query's lowest key are skipped
+    }
 
     // One key tile: issue the next tile's loads into (nk, nv), then compute on (kb, vb).
     auto step = [&](const u16* kb, const u16* vb, u16* nk, u16* nv, int kt) {
@@ -111,8 +122,10 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
         issue_tile<D, kBN, 4>(Kp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nk);
         issue_tile<D, kBN, 4>(Vp + (kbase + kBN) * D, pr.kv_len - kbase - kBN, nv);
       }
-      // Skip the math when the whole tile lies in the future of every query of this wave.
-      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31);
+      // Skip the math when the whole tile lies in the future of every query of this wave, or
+      // below every query's lowest visible key.
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
+                          !(has_lo && kbase + kBN - 1 < wave_lo);
       if (active) {
         // The two 32-key blocks' accumulation chains are interleaved, so that each MFMA's
         // operand read has the other chain's MFMA to hide behind.
@@ -123,18 +136,22 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
           for (int b = 0; b < 2; ++b) s[b] = mfma32(row_operand(kb, b ? ka1 : ka0, kk), qreg[kk], s[b]);
         // Keys past the pair, or after this lane's query in a diagonal pair, are excluded; kmax
         // is the last visible key of the tile (only edge tiles take the masked path).
-        const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first);
+        const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first) ||
+                          (has_lo && kbase < wave_lo_max);
         if (edge) {
           const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
           const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kBN - 1 ? kBN - 1 : lim - kbase));
+          const int kmin = has_lo ? (int)(lo - kbase < 0 ? 0 : (lo - kbase > kBN ? kBN : lo - kbase)) : 0;
           // key of register r in block b is 32 b + perm_reg_row(r, 0) + 8 hh: compare the
-          // compile-time part against kmax - 8 hh
-          const int kmh = kmax - 8 * hh;
+          // compile-time part against kmax - 8 hh and kmin - 8 hh
+          const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (b * 32 + perm_reg_row(r, 0) > kmh) s[b][r] = -__builtin_inff();
+            for (int r = 0; r < 16; ++r) {
+              const int key = b * 32 + perm_reg_row(r, 0);
+              if (key > kmh || key < kml) s[b][r] = -__builtin_inff();
+            }
         }
         float mx = -__builtin_inff();
 #pragma unroll
@@ -186,11 +203,12 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
       __syncthreads();
     };
 
-    issue_tile<D, kBN, 4>(Kp, pr.kv_len, k0);
-    issue_tile<D, kBN, 4>(Vp, pr.kv_len, v0);
+    if (kt0 >= nkt) continue;  // uniform over the workgroup
+    issue_tile<D, kBN, 4>(Kp + kt0 * kBN * D, pr.kv_len - kt0 * kBN, k0);
+    issue_tile<D, kBN, 4>(Vp + kt0 * kBN * D, pr.kv_len - kt0 * kBN, v0);
     wait_vmem();
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
+    for (int kt = (int)kt0; kt < nkt; kt += 2) {
       step(k0, v0, k1, v1, kt);
       if (kt + 1 < nkt) step(k1, v1, k0, v0, kt + 1);
     }

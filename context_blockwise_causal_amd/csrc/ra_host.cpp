@@ -77,6 +77,8 @@ KParams base_params(const Shape& s) {
   kp.D = (int32_t)s.D;
   kp.scale = s.scale;
   kp.scale_log2 = s.scale * 1.4426950408889634f;
+  kp.window = s.window;
+  kp.attn_chunk = s.attn_chunk;
   return kp;
 }
 

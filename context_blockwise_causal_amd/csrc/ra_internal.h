@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <climits>
+
 #include <string>
 
 #include "ra.h"
@@ -19,6 +21,7 @@ struct Shape {
   int64_t B, S, Hq, Hkv, D, n_rep;
   int32_t cp, layout, dtype;
   float scale;      // resolved (never 0)
+  int64_t window, attn_chunk;  // mask restrictions, 0 = off
   int64_t esize;    // bytes per element of the storage dtype
   int64_t chunk;    // rows of one rank slice, S / cp
   int64_t nchunks;  // cp (contiguous) or 2*cp (zigzag)
@@ -63,6 +66,7 @@ struct KRange {
 struct KPair {
   int64_t q_row0, kv_row0, q_len, kv_len;
   int32_t mask, pad_;
+  int64_t q_pos0, kv_pos0;  // sequence positions of the first query / key row
 };
 
 struct KParams {
@@ -83,6 +87,8 @@ struct KParams {
   int32_t B, Hq, Hkv, n_rep, D;
   float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
+  int64_t window;         // sliding window (0 = none)
+  int64_t attn_chunk;     // attention chunk (0 = none)
   int32_t nranges;
   int64_t tiles_per_head;
   KRange ranges[4];
@@ -92,6 +98,31 @@ struct KParams {
 // Builds the range table: groups non-SKIP pairs by their outer range and assigns tiles of
 // `tile_rows` rows.  by_q selects the forward grouping (Q ranges) or the backward (K/V).
 void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64_t tile_rows);
+
+// Lowest key position visible to query position t under the window / chunk restrictions
+// (INT64_MIN when neither is set); the causal bound is key <= t.  constexpr: usable on the
+// host and, implicitly, in device code.
+constexpr int64_t lowest_key(int64_t t, int64_t window, int64_t attn_chunk) {
+  int64_t lo = INT64_MIN;
+  if (window > 0) lo = t - window + 1;
+  if (attn_chunk > 0) {
+    const int64_t c = (t / attn_chunk) * attn_chunk;
+    lo = lo > c ? lo : c;
+  }
+  return lo;
+}
+
+// Highest query position that sees key position j under the window / chunk restrictions
+// (INT64_MAX when neither is set); the causal bound is query >= j.
+constexpr int64_t highest_query(int64_t j, int64_t window, int64_t attn_chunk) {
+  int64_t hi = INT64_MAX;
+  if (window > 0) hi = j + window - 1;
+  if (attn_chunk > 0) {
+    const int64_t c = (j / attn_chunk + 1) * attn_chunk - 1;
+    hi = hi < c ? hi : c;
+  }
+  return hi;
+}
 
 // ---- launchers (kern_*.hip); all return hipError_t as int ----------------------------------
 int launch_chunk_fwd_bf16(const KParams& kp, void* stream);

@@ -45,6 +45,8 @@ ra_status resolve(const ra_problem* p, Shape* out) {
                 (long long)p->seq_len, (long long)nchunks);
   if (!(p->scale >= 0.0f) || isinf(p->scale))
     return fail(RA_ERR_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  if (p->window < 0 || p->attn_chunk < 0)
+    return fail(RA_ERR_INVALID, "window and attn_chunk must be >= 0 (0 = off)");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(RA_ERR_UNSUPPORTED, "head_dim %lld is not supported (64 or 128)",
                 (long long)p->head_dim);
@@ -63,6 +65,8 @@ ra_status resolve(const ra_problem* p, Shape* out) {
   s.layout = p->layout;
   s.dtype = p->dtype;
   s.scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
+  s.window = p->window;
+  s.attn_chunk = p->attn_chunk;
   s.esize = p->dtype == RA_BF16 ? 2 : 4;
   s.chunk = p->seq_len / p->cp_size;
   s.nchunks = nchunks;
@@ -83,6 +87,17 @@ int64_t slice_chunk(const Shape& s, int32_t rank, int32_t which) {
   return c * s.crow;
 }
 
+// A FULL pair whose every key lies below the first query's lowest visible key (window or
+// attention chunk) has no visible key at all: the lowest visible key grows with the query.
+static void restrict_pairs(const Shape& s, ra_pair* pairs, int32_t n) {
+  if (s.window <= 0 && s.attn_chunk <= 0) return;
+  for (int i = 0; i < n; ++i) {
+    ra_pair& p = pairs[i];
+    if (p.mask != RA_MASK_FULL) continue;
+    if (lowest_key(p.q_pos0, s.window, s.attn_chunk) > p.kv_pos0 + p.kv_len - 1) p.mask = RA_MASK_SKIP;
+  }
+}
+
 void plan_step(const Shape& s, int32_t rank, int32_t step, int32_t* owner, ra_pair pairs[4],
                int32_t* n) {
   // Ring direction: K/V move to the next rank each step, so the chunk held at step i was
@@ -90,8 +105,9 @@ void plan_step(const Shape& s, int32_t rank, int32_t step, int32_t* owner, ra_pa
   *owner = (int32_t)(((int64_t)rank - step) % s.cp + s.cp) % s.cp;
   if (s.layout == RA_CONTIGUOUS) {
     const int32_t kind = step == 0 ? RA_MASK_DIAG : (step <= rank ? RA_MASK_FULL : RA_MASK_SKIP);
-    pairs[0] = ra_pair{0, 0, s.chunk, s.chunk, kind, 0};
+    pairs[0] = ra_pair{0, 0, s.chunk, s.chunk, kind, 0, (int64_t)rank * s.chunk, (int64_t)*owner * s.chunk};
     *n = 1;
+    restrict_pairs(s, pairs, *n);
     return;
   }
   // Zigzag: the slice is [chunk r | chunk 2cp-1-r]; the held K/V is [chunk o | chunk 2cp-1-o].
@@ -107,11 +123,14 @@ void plan_step(const Shape& s, int32_t rank, int32_t step, int32_t* owner, ra_pa
   } else {
     ll = RA_MASK_SKIP; lh = RA_MASK_SKIP; hl = RA_MASK_FULL; hh = RA_MASK_FULL;
   }
-  pairs[0] = ra_pair{0, 0, h, h, ll, 0};
-  pairs[1] = ra_pair{0, h, h, h, lh, 0};
-  pairs[2] = ra_pair{h, 0, h, h, hl, 0};
-  pairs[3] = ra_pair{h, h, h, h, hh, 0};
+  const int64_t qlo = (int64_t)rank * h, qhi = (2 * (int64_t)s.cp - 1 - rank) * h;
+  const int64_t klo = (int64_t)*owner * h, khi = (2 * (int64_t)s.cp - 1 - *owner) * h;
+  pairs[0] = ra_pair{0, 0, h, h, ll, 0, qlo, klo};
+  pairs[1] = ra_pair{0, h, h, h, lh, 0, qlo, khi};
+  pairs[2] = ra_pair{h, 0, h, h, hl, 0, qhi, klo};
+  pairs[3] = ra_pair{h, h, h, h, hh, 0, qhi, khi};
   *n = 4;
+  restrict_pairs(s, pairs, *n);
 }
 
 static bool same_or_disjoint(int64_t a0, int64_t al, int64_t b0, int64_t bl) {
@@ -135,6 +154,7 @@ ra_status check_pairs(const ra_pair* pairs, int32_t n, int64_t q_rows, int64_t k
                   (long long)p.kv_row0, (long long)p.kv_len, (long long)kv_rows);
     if (p.mask == RA_MASK_DIAG && p.q_len != p.kv_len)
       return fail(RA_ERR_INVALID, "pair %d: a diagonal pair needs q_len == kv_len", i);
+    if (p.q_pos0 < 0 || p.kv_pos0 < 0) return fail(RA_ERR_INVALID, "pair %d: negative position", i);
   }
   for (int i = 0; i < n; ++i) {
     if (pairs[i].mask == RA_MASK_SKIP) continue;
@@ -206,7 +226,7 @@ void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64
   int nr = 0;
   for (int i = 0; i < n; ++i) {
     const ra_pair& p = pairs[i];
-    kp->pairs[i] = KPair{p.q_row0, p.kv_row0, p.q_len, p.kv_len, p.mask, 0};
+    kp->pairs[i] = KPair{p.q_row0, p.kv_row0, p.q_len, p.kv_len, p.mask, 0, p.q_pos0, p.kv_pos0};
     if (p.mask == RA_MASK_SKIP || p.q_len == 0 || p.kv_len == 0) continue;
     const int64_t r0 = by_q ? p.q_row0 : p.kv_row0;
     const int64_t rl = by_q ? p.q_len : p.kv_len;

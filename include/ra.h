@@ -71,6 +71,13 @@ typedef struct {
   int32_t layout;     /* ra_layout */
   int32_t dtype;      /* ra_dtype */
   float scale;        /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  /* Optional restrictions of the causal mask (the transformers context-parallel page lists
+   * sliding-window and chunked attention among the masks rebuilt over the whole sequence).
+   * With window W > 0 query position t also needs t - j < W of key position j (itself and the
+   * W - 1 keys before it); with attn_chunk C > 0 it needs j / C == t / C (keys of its own
+   * chunk of C positions).  0 disables either. */
+  int64_t window;
+  int64_t attn_chunk;
 } ra_problem;
 
 /* One pair: Q rows [q_row0, q_row0+q_len) of the Q operand against K/V rows
@@ -82,6 +89,11 @@ typedef struct {
   int64_t kv_len;
   int32_t mask;       /* ra_mask */
   int32_t reserved;   /* must be 0 */
+  /* Full-sequence positions of query row q_row0 and key row kv_row0 (rows of a pair are
+   * consecutive positions).  Read only when problem->window or problem->attn_chunk is set;
+   * ra_plan_step fills them. */
+  int64_t q_pos0;
+  int64_t kv_pos0;
 } ra_pair;
 
 typedef struct ra_context ra_context;

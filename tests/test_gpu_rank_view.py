@@ -157,3 +157,47 @@ def test_split_kv_workspace_reuse_and_null_merge_stream(ctx):
     q64, k64, v64 = (t.as_f64(n) for n in ("q", "k", "v"))
     ro, _ = O.rank_view_fwd(q64, k64, v64, 8, "zigzag", 0)
     assert_close(to_f64(outs[1][0]), ro, "bf16", "O split rank 0")
+
+
+MASK_CASES = [
+    # B, chunk rows, Hq, Hkv, D, cp, layout, dtype, window, attn_chunk
+    (1, 256, 4, 2, 128, 4, "contiguous", "bf16", 17, 0),
+    (1, 256, 4, 2, 128, 4, "zigzag", "bf16", 300, 0),
+    (1, 300, 4, 2, 128, 2, "zigzag", "bf16", 0, 100),
+    (2, 256, 3, 3, 64, 4, "contiguous", "bf16", 200, 128),
+    (1, 192, 4, 1, 128, 4, "zigzag", "bf16", 1, 0),
+    (1, 80, 2, 2, 64, 2, "contiguous", "f32", 9, 0),
+    (1, 80, 2, 1, 128, 2, "zigzag", "f32", 0, 24),
+]
+
+
+@pytest.mark.parametrize("B,chunk,Hq,Hkv,D,cp,layout,dtype,window,attn_chunk", MASK_CASES)
+def test_window_and_chunk_masks_match_oracle(ctx, B, chunk, Hq, Hkv, D, cp, layout, dtype, window, attn_chunk):
+    """Sliding-window and chunked-attention masks through the ring and split-KV rank views,
+    forward and backward, every rank."""
+    S = chunk * cp
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype, 0.0, window, attn_chunk)
+    t = draw(B, S, Hq, Hkv, D, dtype, 900 + window + attn_chunk)
+    dev = {n: to_dev(t.store[n], dtype) for n in ("q", "k", "v", "do")}
+    k_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["k"])
+    v_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["v"])
+    q64, k64, v64, do64 = (t.as_f64(n) for n in ("q", "k", "v", "do"))
+    order = O.ring_order(S, cp, layout)
+    for rank in range(cp):
+        q_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["q"])
+        do_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["do"])
+        o, lse = api.rank_view_fwd(ctx, prob, rank, q_sl, k_ring, v_ring, staging=torch.cuda.Stream())
+        o_s, _ = api.rank_view_fwd_split(ctx, prob, rank, q_sl, k_ring, v_ring, merge=torch.cuda.Stream())
+        dq, dk, dv = api.rank_view_bwd(ctx, prob, rank, q_sl, k_ring, v_ring, o, lse, do_sl,
+                                       staging=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        ro, rl = O.rank_view_fwd(q64, k64, v64, cp, layout, rank, None, window, attn_chunk)
+        assert_close(to_f64(o), ro, dtype, f"O rank {rank}")
+        assert_close(to_f64(o_s), ro, dtype, f"O split rank {rank}")
+        assert np.max(np.abs(to_f64(lse) - rl)) < (1e-5 if dtype == "f32" else 2e-3)
+        pos = O.rank_positions(S, cp, layout, rank)
+        rdq, rdk, rdv = O.rank_view_bwd(q64, k64, v64, do64[:, :, pos], cp, layout, rank, None, window,
+                                        attn_chunk)
+        assert_close(to_f64(dq), rdq, dtype, f"dQ rank {rank}")
+        assert_close(to_f64(dk), rdk[:, :, order], dtype, f"dK rank {rank}")
+        assert_close(to_f64(dv), rdv[:, :, order], dtype, f"dV rank {rank}")

@@ -98,3 +98,27 @@ def test_device_entry_points_reject_null_context_without_enqueueing():
     arr = L.pairs_array([(0, 0, 8, 8, L.RA_MASK_DIAG)])
     st = lib.ra_chunk_fwd(None, ctypes.byref(p), None, 8, None, None, 8, arr, 1, None, None, None, None)
     assert st == L.RA_ERR_INVALID
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("cp,window,chunk", [(4, 5, 0), (4, 0, 8), (8, 40, 0), (8, 0, 16), (2, 3, 12)])
+def test_plan_positions_and_window_skips(layout, cp, window, chunk):
+    """Pair positions are the rows' sequence positions; a pair is SKIP exactly when the oracle's
+    visibility (causal, window, attention chunk) has no visible (query, key) in it."""
+    S = 2 * cp * 16
+    prob = api.Problem(1, S, 2, 1, 64, cp, layout, "bf16", 0.0, window, chunk)
+    for rank in range(cp):
+        qpos = O.rank_positions(S, cp, layout, rank)
+        for step in range(cp):
+            owner, pairs = api.ra_plan_step(prob, rank, step, positions=True)
+            kpos = O.rank_positions(S, cp, layout, owner)
+            for q0, k0, ql, kl, mask, qp0, kp0 in pairs:
+                assert np.array_equal(qpos[q0:q0 + ql], np.arange(qp0, qp0 + ql))
+                assert np.array_equal(kpos[k0:k0 + kl], np.arange(kp0, kp0 + kl))
+                vis = O.visible(qpos[q0:q0 + ql], kpos[k0:k0 + kl], window, chunk)
+                causal = O.classify(qpos[q0:q0 + ql], kpos[k0:k0 + kl])
+                if mask == L.RA_MASK_SKIP:
+                    assert not vis.any()
+                else:
+                    assert vis.any()
+                    assert KIND[causal] == mask  # the causal kind is kept; the kernel applies the rest
