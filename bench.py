@@ -27,16 +27,37 @@ METRIC = "attention TFLOP/s fwd+bwd per rank view at 1 GPU; % of bf16 MFMA peak"
 DEFAULT_WORKLOAD = "llama-gqa-cp8-zigzag"
 
 
+def visible_count(q_pos0, kv_pos0, q_len, kv_len, window, attn_chunk):
+    """Number of visible (query, key) pairs of a pair block under the causal mask restricted by
+    a sliding window and / or attention chunks (positions are consecutive in both ranges)."""
+    import numpy as np
+    t = np.arange(q_pos0, q_pos0 + q_len, dtype=np.int64)
+    hi = np.minimum(t, kv_pos0 + kv_len - 1)
+    lo = np.full_like(t, kv_pos0)
+    if window:
+        lo = np.maximum(lo, t - window + 1)
+    if attn_chunk:
+        lo = np.maximum(lo, (t // attn_chunk) * attn_chunk)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
 def counted_flops(api, prob, rank):
-    """Forward FLOPs of one rank view by the metric's counting rule (per ring step)."""
+    """Forward FLOPs of one rank view by the metric's counting rule (per ring step): 4 d L^2 per
+    full pair and 2 d L^2 per diagonal pair; with a sliding window or attention chunks, 4 d per
+    visible (query, key) pair."""
     per_step = []
+    masked = bool(prob.window or prob.attn_chunk)
     for i in range(prob.cp):
-        _, pairs = api.ra_plan_step(prob, rank, i)
+        _, pairs = api.ra_plan_step(prob, rank, i, positions=True)
         f = 0
-        for q0, k0, ql, kl, mask in pairs:
-            if mask == 0:
+        for q0, k0, ql, kl, mask, qp0, kp0 in pairs:
+            if mask == 2:
+                continue
+            if masked:
+                f += 4 * prob.head_dim * visible_count(qp0, kp0, ql, kl, prob.window, prob.attn_chunk)
+            elif mask == 0:
                 f += 4 * prob.head_dim * ql * kl
-            elif mask == 1:
+            else:
                 f += 2 * prob.head_dim * ql * kl
         per_step.append(f * prob.batch * prob.heads_q)
     return per_step
@@ -98,7 +119,7 @@ def chunk_launches(api, prob, wl, k_ring, v_ring):
     for r in wl.ranks:
         flops = counted_flops(api, prob, r)
         for i in range(prob.cp):
-            owner, pairs = api.ra_plan_step(prob, r, i)
+            owner, pairs = api.ra_plan_step(prob, r, i, positions=True)
             if all(p[4] == 2 for p in pairs):
                 continue
             kc = k_ring[:, :, owner * chunk:(owner + 1) * chunk].contiguous()
@@ -235,6 +256,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--same-stream", action="store_true", help="stage K/V on the compute stream")
+    ap.add_argument("--window", type=int, default=0, help="sliding window (0 = plain causal)")
+    ap.add_argument("--attn-chunk", type=int, default=0, help="attention chunk (0 = off)")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only replay the chunk-kernel launches (and one layout gather of K as the "
                          "calibration copy): the program to run under rocprofv3 --pmc")
@@ -263,7 +286,7 @@ def main():
 
     wl = WORKLOADS[args.workload]
     prob = api.Problem(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.cp,
-                       wl.layout, wl.dtype)
+                       wl.layout, wl.dtype, 0.0, args.window, args.attn_chunk)
     t = draw(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.dtype, wl.seed,
              with_grad=True)
     ctx = api.Context(0)
@@ -398,7 +421,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
                    "heads_q": wl.heads_q, "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
                    "cp": wl.cp, "layout": wl.layout, "ranks": list(wl.ranks),
-                   "passes": "fwd+bwd" if wl.backward else "fwd"},
+                   "passes": "fwd+bwd" if wl.backward else "fwd",
+                   "window": args.window, "attn_chunk": args.attn_chunk},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(total_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_of_peak": round(total_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

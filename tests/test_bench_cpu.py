@@ -59,3 +59,25 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert k["fetch_bytes_per_launch"] == pytest.approx(200.0 * 1024 * 2)
     assert k["write_bytes_per_launch"] == pytest.approx(50.0 * 1024)
     assert rec["source_hash"] == bench.source_hash()
+
+
+@pytest.mark.parametrize("window,chunk", [(0, 0), (5, 0), (0, 8), (7, 12), (1, 0)])
+def test_visible_count_matches_oracle_visibility(window, chunk):
+    import numpy as np
+    from oracle import attn64 as O
+    for q0, k0, ql, kl in [(40, 0, 16, 16), (40, 40, 16, 16), (100, 30, 20, 24), (7, 7, 9, 9)]:
+        qp = np.arange(q0, q0 + ql)
+        kp = np.arange(k0, k0 + kl)
+        ref = int(O.visible(qp, kp, window, chunk).sum())
+        assert bench.visible_count(q0, k0, ql, kl, window, chunk) == ref
+
+
+def test_windowed_flops_equal_visible_pairs():
+    """With a window the counted forward FLOPs are 4 d per visible pair, summed over the plan."""
+    import numpy as np
+    from oracle import attn64 as O
+    prob = api.Problem(1, 512, 2, 1, 64, 4, "zigzag", "bf16", 0.0, 40, 0)
+    for rank in range(4):
+        qpos = O.rank_positions(512, 4, "zigzag", rank)
+        vis = O.visible(qpos, np.arange(512), 40, 0).sum()
+        assert sum(bench.counted_flops(api, prob, rank)) == 4 * 64 * vis * 2
