@@ -443,25 +443,38 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 }
 
 template <int D>
-int launch_bwd(const KParams& kv, const KParams& q, void* stream) {
+int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   int e;
   const int64_t nkv = (int64_t)kv.B * kv.Hq * kv.tiles_per_head;
-  if (nkv > 0 && kv.dk) {
+  const int64_t nq = (int64_t)q.B * q.Hq * q.tiles_per_head;
+  const bool do_kv = nkv > 0 && kv.dk, do_q = nq > 0 && q.U;
+  // The two kernels are independent (dK/dV and dQ); with a side stream the dQ kernel runs
+  // beside the dK/dV kernel and the caller's stream waits for both.
+  hipStream_t qs = (hipStream_t)stream;
+  if (fork && do_kv && do_q) {
+    if ((e = (int)hipEventRecord((hipEvent_t)fork->fork, (hipStream_t)stream))) return e;
+    if ((e = (int)hipStreamWaitEvent((hipStream_t)fork->side, (hipEvent_t)fork->fork, 0))) return e;
+    qs = (hipStream_t)fork->side;
+  }
+  if (do_kv) {
     hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
-  const int64_t nq = (int64_t)q.B * q.Hq * q.tiles_per_head;
-  if (nq > 0 && q.U) {
-    hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, (hipStream_t)stream, q);
+  if (do_q) {
+    hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, qs, q);
     if ((e = (int)hipGetLastError())) return e;
+  }
+  if (qs != (hipStream_t)stream) {
+    if ((e = (int)hipEventRecord((hipEvent_t)fork->join, qs))) return e;
+    if ((e = (int)hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)fork->join, 0))) return e;
   }
   return 0;
 }
 
 }  // namespace
 
-int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream) {
-  return kv.D == 128 ? launch_bwd<128>(kv, q, stream) : launch_bwd<64>(kv, q, stream);
+int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
+  return kv.D == 128 ? launch_bwd<128>(kv, q, stream, fork) : launch_bwd<64>(kv, q, stream, fork);
 }
 
 }  // namespace ra

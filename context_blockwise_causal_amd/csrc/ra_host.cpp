@@ -28,6 +28,7 @@ struct ra_context {
   hipStream_t pool[kPoolStreams];
   hipEvent_t done[kMaxSteps];  // chunk i of a split-KV forward has finished
   hipEvent_t fin;              // the split-KV forward's merges and finalize have finished
+  hipEvent_t bfork, bjoin;     // the backward's dQ kernel on a pool stream beside dK/dV
 };
 
 namespace ra {
@@ -91,12 +92,13 @@ int run_fwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* 
   return kp.nranges ? launch_chunk_fwd_f32(kp, stream) : 0;
 }
 
-int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream) {
+int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream,
+            const BwdFork* fork) {
   if (s.dtype == RA_BF16) {
     KParams kq = kp;
     build_ranges(&kp, pairs, n, false, kBwdTileRows);
     build_ranges(&kq, pairs, n, true, kBwdQTileRows);
-    return kp.nranges ? launch_chunk_bwd_bf16(kp, kq, stream) : 0;
+    return kp.nranges ? launch_chunk_bwd_bf16(kp, kq, stream, fork) : 0;
   }
   build_ranges(&kp, pairs, n, true, kF32BwdTileRows);
   return kp.nranges ? launch_chunk_bwd_f32(kp, stream) : 0;
@@ -204,6 +206,8 @@ ra_status ra_create(int32_t device, ra_context** out) {
   for (int i = 0; i < kMaxSteps && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fin, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->bfork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->bjoin, hipEventDisableTiming);
   for (int i = 0; i < kPoolStreams && e == hipSuccess; ++i)
     e = hipStreamCreateWithFlags(&c->pool[i], hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -224,6 +228,8 @@ void ra_destroy(ra_context* c) {
   }
   for (int i = 0; i < kMaxSteps; ++i) (void)hipEventDestroy(c->done[i]);
   (void)hipEventDestroy(c->fin);
+  (void)hipEventDestroy(c->bfork);
+  (void)hipEventDestroy(c->bjoin);
   for (int i = 0; i < kPoolStreams; ++i) (void)hipStreamDestroy(c->pool[i]);
   delete c;
 }
@@ -364,7 +370,8 @@ ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* prob, const void* q, c
   kp.kv_head_rows = kv_rows;
   kp.dkv_head_rows = kv_rows;
   DeviceGuard g(ctx->device);
-  return dev_err(run_bwd(s, kp, pairs, n_pairs, stream), "chunk backward");
+  const BwdFork fork{ctx->pool[0], ctx->bfork, ctx->bjoin};
+  return dev_err(run_bwd(s, kp, pairs, n_pairs, stream, &fork), "chunk backward");
 }
 
 ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* prob, int64_t n, const float* src,
@@ -522,6 +529,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   kp.q = q_slice; kp.dO = dO_slice; kp.lse = lse_slice; kp.delta = delta; kp.U = dq;
   kp.q_head_rows = s.chunk;
   kp.dkv_head_rows = s.S;
+  const BwdFork fork{ctx->pool[0], ctx->bfork, ctx->bjoin};
   auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     kp.k = k; kp.v = v;
@@ -529,7 +537,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     // gradients of owner o's chunk go to its rows of the ring-ordered accumulators
     kp.dk = dk + (int64_t)owner * s.chunk * s.D;
     kp.dv = dv + (int64_t)owner * s.chunk * s.D;
-    return run_bwd(s, kp, pairs, n, cs);
+    return run_bwd(s, kp, pairs, n, cs, &fork);
   };
   if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, step)) != RA_OK)
     return st;

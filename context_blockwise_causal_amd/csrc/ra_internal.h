@@ -127,7 +127,10 @@ constexpr int64_t highest_query(int64_t j, int64_t window, int64_t attn_chunk) {
 // ---- launchers (kern_*.hip); all return hipError_t as int ----------------------------------
 int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
 // Backward as two launches: `kv` has K/V-major ranges (dK, dV), `q` Q-major ranges (dQ).
-int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream);
+// With `fork` the dQ launch goes to fork->side between two events, so the two kernels can run
+// at once; the caller's stream is ordered after both.
+struct BwdFork { void* side; void* fork; void* join; };  // hipStream_t, hipEvent_t, hipEvent_t
+int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
 constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)
