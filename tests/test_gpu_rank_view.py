@@ -201,3 +201,44 @@ def test_window_and_chunk_masks_match_oracle(ctx, B, chunk, Hq, Hkv, D, cp, layo
         assert_close(to_f64(dq), rdq, dtype, f"dQ rank {rank}")
         assert_close(to_f64(dk), rdk[:, :, order], dtype, f"dK rank {rank}")
         assert_close(to_f64(dv), rdv[:, :, order], dtype, f"dV rank {rank}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_scores_and_wide_gqa(ctx, dtype):
+    """Softmax scale 1 (scores of standard deviation ~ sqrt(D)): the running max moves by far
+    more than the lazy-rescale threshold between tiles and chunks, so the rescale path and
+    near one-hot rows are exercised; 16 query heads share one key/value head."""
+    B, Hq, Hkv, D, cp, layout = 1, 16, 1, 128 if dtype == "bf16" else 64, 4, "zigzag"
+    chunk = 256 if dtype == "bf16" else 64
+    S = chunk * cp
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype, 1.0)
+    t = draw(B, S, Hq, Hkv, D, dtype, 4242)
+    dev = {n: to_dev(t.store[n], dtype) for n in ("q", "k", "v", "do")}
+    k_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["k"])
+    v_ring = api.ra_layout_gather(ctx, prob, 0, cp, dev["v"])
+    q64, k64, v64, do64 = (t.as_f64(n) for n in ("q", "k", "v", "do"))
+    order = O.ring_order(S, cp, layout)
+    for rank in (0, cp - 1):
+        q_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["q"])
+        do_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["do"])
+        o, lse = api.rank_view_fwd(ctx, prob, rank, q_sl, k_ring, v_ring, staging=torch.cuda.Stream())
+        dq, dk, dv = api.rank_view_bwd(ctx, prob, rank, q_sl, k_ring, v_ring, o, lse, do_sl,
+                                       staging=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        ro, rl = O.rank_view_fwd(q64, k64, v64, cp, layout, rank, 1.0)
+        if dtype == "bf16":
+            assert_close(to_f64(o), ro, dtype, f"O rank {rank}")
+        else:
+            # fp32: the rounding error of a score grows with its size; with the scale sqrt(D)
+            # times the default, so does the bound (1e-5 at the default scale)
+            err = np.max(np.abs(to_f64(o) - ro))
+            assert err <= 1e-5 * np.sqrt(D), (rank, err)
+        assert np.max(np.abs(to_f64(lse) - rl)) < (1e-4 if dtype == "f32" else 2e-2)
+        pos = O.rank_positions(S, cp, layout, rank)
+        rdq, rdk, rdv = O.rank_view_bwd(q64, k64, v64, do64[:, :, pos], cp, layout, rank, 1.0)
+        # gradients carry the scale (1 here, ~11x the default): compare relative to their size
+        for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk[:, :, order], "dK"), (dv, rdv[:, :, order], "dV")):
+            g, r = to_f64(got), ref
+            rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+            assert rel < (1e-5 if dtype == "f32" else 1e-2), (name, rank, rel)
+            assert np.all(np.isfinite(g))
