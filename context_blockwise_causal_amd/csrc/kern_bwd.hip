@@ -44,42 +44,55 @@ struct KvCfg {
   static constexpr int QT = kKvBQ * D;  // elements of one Q (or dO) tile
 };
 
-// lse for threads 0..31 and delta for threads 32..63 of a query step, one value per thread,
-// loaded raw (row index clamped into the pair) so that nothing waits on the load before the
-// store at the end of the step.
-__device__ __forceinline__ float kv_load_extra(const float* __restrict__ lse, const float* __restrict__ dlt,
-                                               int64_t q0, int64_t q_len) {
-  const int t = threadIdx.x;
-  float x = 0.f;
-  if (t < 2 * kKvBQ) {
-    const int64_t q = q0 + (t & (kKvBQ - 1));
-    x = (t < kKvBQ ? lse : dlt)[q < q_len ? q : q_len - 1];
-  }
-  return x;
+// Raw lse and delta of the step row that accumulator register (lane & 15) holds in this lane's
+// half (row index clamped into the pair): lanes 16 c .. 16 c + 15 of each 16-lane DPP row hold
+// the 16 values its lanes need, handed out per register by a row broadcast.
+__device__ __forceinline__ void kv_load_rows(const float* __restrict__ lse, const float* __restrict__ dlt,
+                                             int64_t q0, int64_t q_len, float& a, float& d) {
+  const int l = threadIdx.x & 63;
+  const int64_t q = q0 + perm_reg_row(l & 15, l >> 5);
+  const int64_t qc = q < q_len ? q : q_len - 1;
+  a = lse[qc];
+  d = dlt[qc];
 }
 
-// Stores the step's lse in base 2 (+inf for rows past the pair, so their probabilities vanish)
-// and delta (0 past the pair).
-__device__ __forceinline__ void kv_store_extra(float* __restrict__ ex, float x, int64_t q0, int64_t q_len) {
-  const int t = threadIdx.x;
-  if (t < 2 * kKvBQ) {
-    const bool valid = q0 + (t & (kKvBQ - 1)) < q_len;
-    ex[t] = t < kKvBQ ? (valid ? x * kLog2e : __builtin_inff()) : (valid ? x : 0.f);
+// Value of lane 16 (lane / 16) + r: DPP row_newbcast.
+__device__ __forceinline__ float row_bcast(float x, int r) {
+  const int v = __builtin_bit_cast(int, x);
+  int o;
+  switch (r) {
+    case 0: o = __builtin_amdgcn_mov_dpp(v, 0x150, 0xF, 0xF, false); break;
+    case 1: o = __builtin_amdgcn_mov_dpp(v, 0x151, 0xF, 0xF, false); break;
+    case 2: o = __builtin_amdgcn_mov_dpp(v, 0x152, 0xF, 0xF, false); break;
+    case 3: o = __builtin_amdgcn_mov_dpp(v, 0x153, 0xF, 0xF, false); break;
+    case 4: o = __builtin_amdgcn_mov_dpp(v, 0x154, 0xF, 0xF, false); break;
+    case 5: o = __builtin_amdgcn_mov_dpp(v, 0x155, 0xF, 0xF, false); break;
+    case 6: o = __builtin_amdgcn_mov_dpp(v, 0x156, 0xF, 0xF, false); break;
+    case 7: o = __builtin_amdgcn_mov_dpp(v, 0x157, 0xF, 0xF, false); break;
+    case 8: o = __builtin_amdgcn_mov_dpp(v, 0x158, 0xF, 0xF, false); break;
+    case 9: o = __builtin_amdgcn_mov_dpp(v, 0x159, 0xF, 0xF, false); break;
+    case 10: o = __builtin_amdgcn_mov_dpp(v, 0x15A, 0xF, 0xF, false); break;
+    case 11: o = __builtin_amdgcn_mov_dpp(v, 0x15B, 0xF, 0xF, false); break;
+    case 12: o = __builtin_amdgcn_mov_dpp(v, 0x15C, 0xF, 0xF, false); break;
+    case 13: o = __builtin_amdgcn_mov_dpp(v, 0x15D, 0xF, 0xF, false); break;
+    case 14: o = __builtin_amdgcn_mov_dpp(v, 0x15E, 0xF, 0xF, false); break;
+    default: o = __builtin_amdgcn_mov_dpp(v, 0x15F, 0xF, 0xF, false); break;
   }
+  return __builtin_bit_cast(float, o);
 }
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   using C = KvCfg<D>;
-  // The V tile and two buffers of (Q, dO, lse|delta), carved out of one LDS array.  Each step
+  // The V tile and two buffers of (Q, dO), carved out of one LDS array (lse and delta travel in
+  // registers and reach their lanes by DPP row broadcasts, see kv_load_rows).  Each step
   // reads one buffer while direct loads fill the other; the step takes every LDS pointer as a
   // __restrict__ parameter, which lets the compiler prove that those loads do not alias its reads
   // (so it does not wait for them before the step's LDS reads).  One array, not several: with
   // several LDS variables the compiler's LDS lowering replaces the pointer-based alias scopes.
-  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT + 8 * kKvBQ];
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT];
   u16* const vt = lds;
   u16* const qdbuf = lds + kKvBN * D;
-  float* const exbuf = reinterpret_cast<float*>(lds + kKvBN * D + 4 * C::QT);
 
   const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -139,15 +152,19 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const float* dltp = p.delta + qhead + pr.q_row0;
 
     // One query step on (Qs, dOs, ex); the next step's rows go into (nQ, ndO, nex).
+    // (la, ld): raw lse / delta of this step's rows, loaded one step ahead.
+    float la, ld;
     auto step = [&](const u16* __restrict__ Vs, const u16* __restrict__ Qs, const u16* __restrict__ dOs,
-                    const float* __restrict__ ex, u16* __restrict__ nQ, u16* __restrict__ ndO,
-                    float* __restrict__ nex, int it) {
+                    u16* __restrict__ nQ, u16* __restrict__ ndO, int it) {
       const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
-      float extra = 0.f;
+      // this lane's broadcast values: lse in base 2 (+inf past the pair, so that P vanishes) and
+      // delta (0 past the pair)
+      const bool rv = qbase + perm_reg_row(lane & 15, hh) < pr.q_len;
+      const float lse2 = rv ? la * kLog2e : __builtin_inff(), dlt = rv ? ld : 0.f;
       if (it + 1 < niter) {
         issue_tile<D, kKvBQ, 4>(Qp + (qbase + kKvBQ) * D, pr.q_len - qbase - kKvBQ, nQ);
         issue_tile<D, kKvBQ, 4>(dOp + (qbase + kKvBQ) * D, pr.q_len - qbase - kKvBQ, ndO);
-        extra = kv_load_extra(lsep, dltp, qbase + kKvBQ, pr.q_len);
+        kv_load_rows(lsep, dltp, qbase + kKvBQ, pr.q_len, la, ld);
       }
       // The whole wavefront lies in the future of every query of this step (diagonal pairs).
       const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1) && !(has_hi && qbase > wave_hi_max);
@@ -168,21 +185,11 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         // query of register 4j+i is perm_reg_row(4j+i, 0) + 8 hh: compare the compile-time part
         // against the bounds shifted by 8 hh
         const int qml = qmin - 8 * hh, qmh = qmax - 8 * hh;
-        const float* lse2s = ex;
-        const float* dlts = ex + kKvBQ;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // registers 4j..4j+3 hold queries perm_reg_row(4j+i, hh): 4 consecutive rows
-          const int r0 = perm_reg_row(4 * j, hh);
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + r0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i;
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -l4[i]));
-            s[r] = pv;
-            dp[r] = (pv * p.scale) * (dp[r] - d4[i]);  // scale * dS
-          }
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -row_bcast(lse2, r)));
+          s[r] = pv;
+          dp[r] = (pv * p.scale) * (dp[r] - row_bcast(dlt, r));  // scale * dS
         }
         if (edge) {  // excluded (key, query) pairs get P = dS = 0
 #pragma unroll
@@ -215,22 +222,19 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
             dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
       }
-      if (it + 1 < niter) kv_store_extra(nex, extra, qbase + kKvBQ, pr.q_len);
       wait_vmem();
       __syncthreads();
     };
 
     issue_tile<D, kKvBQ, 4>(Qp + q_begin * D, pr.q_len - q_begin, qdbuf);
     issue_tile<D, kKvBQ, 4>(dOp + q_begin * D, pr.q_len - q_begin, qdbuf + C::QT);
-    kv_store_extra(exbuf, kv_load_extra(lsep, dltp, q_begin, pr.q_len), q_begin, pr.q_len);
+    kv_load_rows(lsep, dltp, q_begin, pr.q_len, la, ld);
     wait_vmem();
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
       u16* cur = qdbuf + (it & 1) * 2 * C::QT;
       u16* nxt = qdbuf + ((it + 1) & 1) * 2 * C::QT;
-      float* ecur = exbuf + (it & 1) * 2 * kKvBQ;
-      float* enxt = exbuf + ((it + 1) & 1) * 2 * kKvBQ;
-      step(vt, cur, cur + C::QT, ecur, nxt, nxt + C::QT, enxt, it);
+      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, it);
     }
   }
 
