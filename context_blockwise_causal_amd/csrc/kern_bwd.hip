@@ -468,7 +468,7 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
     hipLaunchKernelGGL(chunk_bwd_q_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, qs, q);
     if ((e = (int)hipGetLastError())) return e;
   }
-  if (qs != (hipStream_t)stream) {
+  if (qs != (hipStream_t)stream && fork->join) {
     if ((e = (int)hipEventRecord((hipEvent_t)fork->join, qs))) return e;
     if ((e = (int)hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)fork->join, 0))) return e;
   }

@@ -29,6 +29,7 @@ struct ra_context {
   hipEvent_t done[kMaxSteps];  // chunk i of a split-KV forward has finished
   hipEvent_t fin;              // the split-KV forward's merges and finalize have finished
   hipEvent_t bfork, bjoin;     // the backward's dQ kernel on a pool stream beside dK/dV
+  hipEvent_t qfreed[2];        // the backward ring's dQ kernels have finished reading a slot
 };
 
 namespace ra {
@@ -111,11 +112,13 @@ bool any_compute(const ra_pair* pairs, int32_t n) {
 }
 
 // The ring loop shared by both passes.  `step_fn(step, kv_k, kv_v, kv_head_rows, owner,
-// pairs, n)` enqueues one step's compute on the compute stream.
+// pairs, n)` enqueues one step's compute on the compute stream and, when `side` is not NULL,
+// part of it on `side`, which the caller joins after the loop: a slot is refilled only once the
+// work of both streams that reads it has finished.
 template <class StepFn>
 ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k_ring,
                     const void* v_ring, char* slot0, char* slot1, hipStream_t cs, hipStream_t ss,
-                    StepFn step_fn) {
+                    hipStream_t side, StepFn step_fn) {
   struct Step { int32_t i, owner, n; ra_pair pairs[4]; };
   Step staged[64];
   int nstaged = 0;
@@ -144,6 +147,8 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   auto issue_copy = [&](int k) -> ra_status {
     const int sl = k & 1;
     if (k >= 2 && (e = (int)hipStreamWaitEvent(ss, ctx->freed[sl], 0))) return dev_err(e, "wait slot_free");
+    if (k >= 2 && side && (e = (int)hipStreamWaitEvent(ss, ctx->qfreed[sl], 0)))
+      return dev_err(e, "wait slot_free (side)");
     const int64_t off = (int64_t)staged[k].owner * chunk_bytes;
     if ((e = launch_copy2d((const char*)k_ring + off, head_bytes, slots[sl], chunk_bytes, chunk_bytes,
                            s.B * s.Hkv, ss)))
@@ -176,6 +181,7 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
                      staged[k].n)))
       return dev_err(e, "chunk kernel (staged step)");
     if ((e = (int)hipEventRecord(ctx->freed[sl], cs))) return dev_err(e, "record slot_free");
+    if (side && (e = (int)hipEventRecord(ctx->qfreed[sl], side))) return dev_err(e, "record slot_free (side)");
   }
   return RA_OK;
 }
@@ -202,6 +208,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
   for (int i = 0; i < 2 && e == hipSuccess; ++i) {
     e = hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->freed[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->qfreed[i], hipEventDisableTiming);
   }
   for (int i = 0; i < kMaxSteps && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming);
@@ -225,6 +232,7 @@ void ra_destroy(ra_context* c) {
   for (int i = 0; i < 2; ++i) {
     (void)hipEventDestroy(c->ready[i]);
     (void)hipEventDestroy(c->freed[i]);
+    (void)hipEventDestroy(c->qfreed[i]);
   }
   for (int i = 0; i < kMaxSteps; ++i) (void)hipEventDestroy(c->done[i]);
   (void)hipEventDestroy(c->fin);
@@ -420,7 +428,7 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     kp.dkv_head_rows = kv_head_rows;
     return run_fwd(s, kp, pairs, n, cs);
   };
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, step)) != RA_OK)
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr, step)) != RA_OK)
     return st;
   return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
                  "forward finalize");
@@ -529,7 +537,12 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   kp.q = q_slice; kp.dO = dO_slice; kp.lse = lse_slice; kp.delta = delta; kp.U = dq;
   kp.q_head_rows = s.chunk;
   kp.dkv_head_rows = s.S;
-  const BwdFork fork{ctx->pool[0], ctx->bfork, ctx->bjoin};
+  // The dQ kernels run on a pool stream beside the dK/dV kernels and are joined once, after the
+  // ring: a step's dK/dV kernel can start while the previous step's dQ kernel drains.  The dQ
+  // kernels stay in order on their stream (each adds into the same dq rows) and the dK/dV
+  // kernels on the compute stream (their steps write different owners' rows).
+  hipStream_t side = ctx->pool[0];
+  const BwdFork fork{side, ctx->bfork, nullptr};
   auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     kp.k = k; kp.v = v;
@@ -539,8 +552,10 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     kp.dv = dv + (int64_t)owner * s.chunk * s.D;
     return run_bwd(s, kp, pairs, n, cs, &fork);
   };
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, step)) != RA_OK)
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side, step)) != RA_OK)
     return st;
+  if ((e = (int)hipEventRecord(ctx->bjoin, side))) return dev_err(e, "record dq join");
+  if ((e = (int)hipStreamWaitEvent(cs, ctx->bjoin, 0))) return dev_err(e, "wait dq join");
   if ((e = launch_cast_from_f32(rows * s.D, s.dtype, dq, dq_slice, cs))) return dev_err(e, "cast dq");
   if ((e = launch_cast_from_f32(kvel, s.dtype, dk, dk_ring, cs))) return dev_err(e, "cast dk");
   if ((e = launch_cast_from_f32(kvel, s.dtype, dv, dv_ring, cs))) return dev_err(e, "cast dv");

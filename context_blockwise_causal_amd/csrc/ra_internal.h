@@ -129,7 +129,9 @@ int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
 // Backward as two launches: `kv` has K/V-major ranges (dK, dV), `q` Q-major ranges (dQ).
 // With `fork` the dQ launch goes to fork->side between two events, so the two kernels can run
 // at once; the caller's stream is ordered after both.
-struct BwdFork { void* side; void* fork; void* join; };  // hipStream_t, hipEvent_t, hipEvent_t
+// The dQ kernel on `side` beside the dK/dV kernel (hipStream_t, hipEvent_t, hipEvent_t).  With
+// join == nullptr the caller's stream does not wait for it: the caller joins later.
+struct BwdFork { void* side; void* fork; void* join; };
 int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
