@@ -30,6 +30,7 @@ struct ra_context {
   hipEvent_t fin;              // the split-KV forward's merges and finalize have finished
   hipEvent_t bfork, bjoin;     // the backward's dQ kernel on a pool stream beside dK/dV
   hipEvent_t qfreed[2];        // the backward ring's dQ kernels have finished reading a slot
+  hipEvent_t ajoin;            // the ring's second compute stream has finished
 };
 
 namespace ra {
@@ -111,14 +112,16 @@ bool any_compute(const ra_pair* pairs, int32_t n) {
   return false;
 }
 
-// The ring loop shared by both passes.  `step_fn(step, kv_k, kv_v, kv_head_rows, owner,
-// pairs, n)` enqueues one step's compute on the compute stream and, when `side` is not NULL,
-// part of it on `side`, which the caller joins after the loop: a slot is refilled only once the
-// work of both streams that reads it has finished.
+// The ring loop shared by both passes.  `step_fn(stream, kv_k, kv_v, kv_head_rows, owner,
+// pairs, n)` enqueues one step's compute on `stream` and, when `side` is not NULL, part of it on
+// `side`, which the caller joins after the loop.  With `alt` set, the steps staged in slot 1 run
+// on `alt` instead of the compute stream (only for steps that do not depend on each other); the
+// loop joins `alt` into the compute stream before it returns.  A slot is refilled only once all
+// the work that reads it has finished.
 template <class StepFn>
 ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k_ring,
                     const void* v_ring, char* slot0, char* slot1, hipStream_t cs, hipStream_t ss,
-                    hipStream_t side, StepFn step_fn) {
+                    hipStream_t side, hipStream_t alt, StepFn step_fn) {
   struct Step { int32_t i, owner, n; ra_pair pairs[4]; };
   Step staged[64];
   int nstaged = 0;
@@ -161,27 +164,36 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   };
 
   ra_status st;
-  if (nstaged > 0 && ss != cs) {
-    // The slots may still be read by earlier work on the compute stream.
+  const bool use_alt = alt && alt != cs && nstaged > 1;
+  hipStream_t kvs[2] = {cs, use_alt ? alt : cs};
+  if ((nstaged > 0 && ss != cs) || use_alt) {
+    // The slots may still be read by earlier work on the compute stream, and the second compute
+    // stream starts after everything the caller queued before the loop.
     if ((e = (int)hipEventRecord(ctx->start, cs))) return dev_err(e, "record start");
-    if ((e = (int)hipStreamWaitEvent(ss, ctx->start, 0))) return dev_err(e, "wait start");
+    if (nstaged > 0 && ss != cs && (e = (int)hipStreamWaitEvent(ss, ctx->start, 0))) return dev_err(e, "wait start");
+    if (use_alt && (e = (int)hipStreamWaitEvent(alt, ctx->start, 0))) return dev_err(e, "wait start (alt)");
   }
   if (nstaged > 0 && (st = issue_copy(0)) != RA_OK) return st;
   if (have_local) {
     const int64_t off = (int64_t)rank * chunk_bytes;
-    if ((e = step_fn((const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
+    if ((e = step_fn(cs, (const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
                      local.pairs, local.n)))
       return dev_err(e, "chunk kernel (local step)");
   }
   for (int k = 0; k < nstaged; ++k) {
     if (k + 1 < nstaged && (st = issue_copy(k + 1)) != RA_OK) return st;
     const int sl = k & 1;
-    if ((e = (int)hipStreamWaitEvent(cs, ctx->ready[sl], 0))) return dev_err(e, "wait slot_ready");
-    if ((e = step_fn(slots[sl], slots[sl] + slot_half, s.chunk, staged[k].owner, staged[k].pairs,
+    const hipStream_t t = kvs[sl];
+    if ((e = (int)hipStreamWaitEvent(t, ctx->ready[sl], 0))) return dev_err(e, "wait slot_ready");
+    if ((e = step_fn(t, slots[sl], slots[sl] + slot_half, s.chunk, staged[k].owner, staged[k].pairs,
                      staged[k].n)))
       return dev_err(e, "chunk kernel (staged step)");
-    if ((e = (int)hipEventRecord(ctx->freed[sl], cs))) return dev_err(e, "record slot_free");
+    if ((e = (int)hipEventRecord(ctx->freed[sl], t))) return dev_err(e, "record slot_free");
     if (side && (e = (int)hipEventRecord(ctx->qfreed[sl], side))) return dev_err(e, "record slot_free (side)");
+  }
+  if (use_alt) {
+    if ((e = (int)hipEventRecord(ctx->ajoin, alt))) return dev_err(e, "record alt join");
+    if ((e = (int)hipStreamWaitEvent(cs, ctx->ajoin, 0))) return dev_err(e, "wait alt join");
   }
   return RA_OK;
 }
@@ -210,6 +222,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->freed[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->qfreed[i], hipEventDisableTiming);
   }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ajoin, hipEventDisableTiming);
   for (int i = 0; i < kMaxSteps && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fin, hipEventDisableTiming);
@@ -234,6 +247,7 @@ void ra_destroy(ra_context* c) {
     (void)hipEventDestroy(c->freed[i]);
     (void)hipEventDestroy(c->qfreed[i]);
   }
+  (void)hipEventDestroy(c->ajoin);
   for (int i = 0; i < kMaxSteps; ++i) (void)hipEventDestroy(c->done[i]);
   (void)hipEventDestroy(c->fin);
   (void)hipEventDestroy(c->bfork);
@@ -420,15 +434,16 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   KParams kp = base_params(s);
   kp.q = q_slice; kp.U = U; kp.m = m; kp.l = l;
   kp.q_head_rows = s.chunk;
-  auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
+  auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     (void)owner;
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
     kp.dkv_head_rows = kv_head_rows;
-    return run_fwd(s, kp, pairs, n, cs);
+    return run_fwd(s, kp, pairs, n, t);
   };
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr, step)) != RA_OK)
+  // every step folds into the same state: one compute stream
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr, nullptr, step)) != RA_OK)
     return st;
   return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
                  "forward finalize");
@@ -539,20 +554,23 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   kp.dkv_head_rows = s.S;
   // The dQ kernels run on a pool stream beside the dK/dV kernels and are joined once, after the
   // ring: a step's dK/dV kernel can start while the previous step's dQ kernel drains.  The dQ
-  // kernels stay in order on their stream (each adds into the same dq rows) and the dK/dV
-  // kernels on the compute stream (their steps write different owners' rows).
+  // kernels stay in order on their stream (each adds into the same dq rows).  The dK/dV kernels
+  // of different steps write different owners' rows, so in the bf16 path the steps staged in
+  // slot 1 run theirs on a second pool stream, beside those of the compute stream.
   hipStream_t side = ctx->pool[0];
   const BwdFork fork{side, ctx->bfork, nullptr};
-  auto step = [&](const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
+  auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
     // gradients of owner o's chunk go to its rows of the ring-ordered accumulators
     kp.dk = dk + (int64_t)owner * s.chunk * s.D;
     kp.dv = dv + (int64_t)owner * s.chunk * s.D;
-    return run_bwd(s, kp, pairs, n, cs, &fork);
+    return run_bwd(s, kp, pairs, n, t, &fork);
   };
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side, step)) != RA_OK)
+  // (the fp32 path adds dQ inside its single kernel: its steps stay on one stream)
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side,
+                      s.dtype == RA_BF16 ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
   if ((e = (int)hipEventRecord(ctx->bjoin, side))) return dev_err(e, "record dq join");
   if ((e = (int)hipStreamWaitEvent(cs, ctx->bjoin, 0))) return dev_err(e, "wait dq join");
