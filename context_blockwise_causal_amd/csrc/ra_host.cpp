@@ -112,6 +112,18 @@ bool any_compute(const ra_pair* pairs, int32_t n) {
   return false;
 }
 
+// Ring steps after the local one that have work (the steps the ring loop stages).
+int staged_steps(const Shape& s, int32_t rank) {
+  int n = 0;
+  for (int32_t i = 1; i < s.cp; ++i) {
+    int32_t owner, np;
+    ra_pair pairs[4];
+    plan_step(s, rank, i, &owner, pairs, &np);
+    if (any_compute(pairs, np)) ++n;
+  }
+  return n;
+}
+
 // The ring loop shared by both passes.  `step_fn(stream, kv_k, kv_v, kv_head_rows, owner,
 // pairs, n)` enqueues one step's compute on `stream` and, when `side` is not NULL, part of it on
 // `side`, which the caller joins after the loop.  With `alt` set, the steps staged in slot 1 run
@@ -430,21 +442,34 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   DeviceGuard g(ctx->device);
   int e;
   const int64_t rows = s.B * s.Hq * s.chunk;
+  // Consecutive steps fold into the same rows, so one running state would chain every step's
+  // kernel to the previous one.  With two or more staged steps, the steps staged in slot 1 fold
+  // into a second state on a second stream, concurrently with the others, and the two states
+  // are merged after the ring (online softmax is exact in any grouping).  Which state a step
+  // uses depends only on its slot, so the result does not depend on timing.
+  const bool two = W.two && staged_steps(s, rank) >= 2;
+  float* U2 = reinterpret_cast<float*>(ws + W.U2);
+  float* m2 = reinterpret_cast<float*>(ws + W.m2);
+  float* l2 = reinterpret_cast<float*>(ws + W.l2);
   if ((e = launch_state_init(rows, s.D, U, m, l, cs))) return dev_err(e, "state init");
+  if (two && (e = launch_state_init(rows, s.D, U2, m2, l2, cs))) return dev_err(e, "state init");
   KParams kp = base_params(s);
-  kp.q = q_slice; kp.U = U; kp.m = m; kp.l = l;
+  kp.q = q_slice;
   kp.q_head_rows = s.chunk;
   auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     (void)owner;
+    const bool b = t != cs;  // slot-1 steps run on the second stream
+    kp.U = b ? U2 : U; kp.m = b ? m2 : m; kp.l = b ? l2 : l;
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
     kp.dkv_head_rows = kv_head_rows;
     return run_fwd(s, kp, pairs, n, t);
   };
-  // every step folds into the same state: one compute stream
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr, nullptr, step)) != RA_OK)
+  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr,
+                      two ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
+  if (two && (e = launch_state_merge(rows, s.D, U2, m2, l2, U, m, l, cs))) return dev_err(e, "state merge");
   return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
                  "forward finalize");
 }

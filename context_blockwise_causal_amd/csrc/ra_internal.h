@@ -43,7 +43,10 @@ void plan_step(const Shape& s, int32_t rank, int32_t step, int32_t* owner, ra_pa
 int64_t slice_chunk(const Shape& s, int32_t rank, int32_t which);
 
 // Workspace carve-up, shared by ra_workspace_size and the rank-view drivers.
-struct FwdWs { size_t U, m, l, slot[2], total; };
+// Forward: the running state; with two staging slots a second state (U2, m2, l2) for the steps
+// staged in slot 1, merged into the first after the ring (two states let consecutive steps run
+// concurrently); then the slots.
+struct FwdWs { size_t U, m, l, U2, m2, l2, slot[2], total; bool two; };
 struct BwdWs { size_t dq, dk, dv, delta, slot[2], total; };
 FwdWs fwd_ws(const Shape& s);
 // Split-KV forward: the running state, then one partial state per ring step (cp of them).
@@ -127,10 +130,9 @@ constexpr int64_t highest_query(int64_t j, int64_t window, int64_t attn_chunk) {
 // ---- launchers (kern_*.hip); all return hipError_t as int ----------------------------------
 int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
 // Backward as two launches: `kv` has K/V-major ranges (dK, dV), `q` Q-major ranges (dQ).
-// With `fork` the dQ launch goes to fork->side between two events, so the two kernels can run
-// at once; the caller's stream is ordered after both.
-// The dQ kernel on `side` beside the dK/dV kernel (hipStream_t, hipEvent_t, hipEvent_t).  With
-// join == nullptr the caller's stream does not wait for it: the caller joins later.
+// With `fork` (hipStream_t side, hipEvent_t fork, hipEvent_t join) the dQ launch goes to `side`
+// after a fork event, so the two kernels can run at once, and the caller's stream then waits
+// for it through `join`; with join == nullptr it does not, and the caller joins later.
 struct BwdFork { void* side; void* fork; void* join; };
 int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);

@@ -180,6 +180,10 @@ FwdWs fwd_ws(const Shape& s) {
   w.U = off; off += align256(rows * s.D * 4);
   w.m = off; off += align256(rows * 4);
   w.l = off; off += align256(rows * 4);
+  w.two = nslots == 2;
+  w.U2 = off; if (w.two) off += align256(rows * s.D * 4);
+  w.m2 = off; if (w.two) off += align256(rows * 4);
+  w.l2 = off; if (w.two) off += align256(rows * 4);
   for (int i = 0; i < 2; ++i) {
     w.slot[i] = off;
     if (i < nslots) off += align256(slot);

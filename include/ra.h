@@ -238,7 +238,11 @@ ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* problem, int64_t n
  * For step i = 0..cp-1 the chunk of owner (rank - i) mod cp is copied into one of two
  * workspace slots on `staging` (the stand-in for the ring receive) while step i-1 computes on
  * `compute`; events order slot reuse.  A step whose pairs are all SKIP neither stages nor
- * computes.  Workspace: ra_workspace_size(problem, 0).  compute and staging may be equal. */
+ * computes.  With two or more staged steps, those staged in slot 1 fold into a second running
+ * state on a context stream, concurrently with the other steps, and the two states are merged
+ * before the finalize; which state a step uses depends only on its slot, so the result is the
+ * same for any timing.  All work is ordered before later work on `compute`.
+ * Workspace: ra_workspace_size(problem, 0).  compute and staging may be equal. */
 ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* problem, int32_t rank,
                            const void* q_slice, const void* k_ring, const void* v_ring,
                            void* o_slice, float* lse_slice, void* workspace,
@@ -265,6 +269,12 @@ ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* problem, int
  * (batch, heads_kv, S, head_dim) in owner-major ring order: this rank's contribution to every
  * owner's K/V gradient (rows of chunks this rank never attends to are zero); summing dk_ring
  * over all ranks gives the full-sequence gradient -- the ring's return-to-owner.
+ * Staging and slot reuse as for the forward.  In the bf16 path each step's dQ kernel runs on a
+ * context stream (in step order: the steps add into the same dQ rows) and the dK/dV kernels of
+ * the steps staged in slot 1 on a second one (steps write different owners' rows); both are
+ * joined into `compute` before the final casts, so all work is ordered before later work on
+ * `compute`.  dK/dV sums over the query heads of a group use fp32 atomics, whose order (and so
+ * the last bits of dk_ring, dv_ring) can vary from run to run.
  * Workspace: ra_workspace_size(problem, 1). */
 ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* problem, int32_t rank,
                            const void* q_slice, const void* k_ring, const void* v_ring,

@@ -49,10 +49,14 @@ def test_workspace_sizes():
     p = api.Problem(2, 4096, 12, 4, 64, 4, "contiguous", "bf16")
     rows = 2 * 12 * 1024
     slot = 2 * 4 * 1024 * 64 * 2 * 2
-    assert api.ra_workspace_size(p, 0) == rows * 64 * 4 + 2 * rows * 4 + 2 * slot
+    state = rows * 64 * 4 + 2 * rows * 4
+    assert api.ra_workspace_size(p, 0) == 2 * state + 2 * slot  # two states with two slots
     kvel = 2 * 4 * 4096 * 64
     assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot
     assert api.ra_workspace_size(p, 2) == (1 + 4) * (rows * 64 * 4 + 2 * rows * 4)  # running + 4 partials
+    two = api.Problem(2, 4096, 12, 4, 64, 2, "contiguous", "bf16")  # one staging slot, one state
+    rows2 = 2 * 12 * 2048
+    assert api.ra_workspace_size(two, 0) == rows2 * 64 * 4 + 2 * rows2 * 4 + 2 * 4 * 2048 * 64 * 2 * 2
     one = api.Problem(1, 512, 2, 2, 128, 1, "contiguous", "f32")
     assert api.ra_workspace_size(one, 0) == 2 * 512 * 128 * 4 + 2 * 4096  # no staging slots at cp=1
 
