@@ -194,16 +194,23 @@ struct TileRef {
   int nrows;     // rows of the tile inside its range (<= tile rows)
 };
 
-// Maps the hardware workgroup index to (batch, head, tile).  Workgroup i is dispatched to
-// XCD i % 8; each XCD is given one contiguous run of the logical order so that the query
-// heads sharing a key/value head (adjacent in the logical order) meet in the same L2.  The
-// logical order is batch, head (kv-head major), then tiles heaviest first.
+// Maps the hardware workgroup index to (batch, head, tile).  The logical order is batch, head
+// (kv-head major), then tiles heaviest first.  Workgroup i is dispatched to XCD i % 8.  When the
+// heads split evenly over the 8 XCDs, each XCD is given one contiguous run of the logical order
+// (whole heads), so that the query heads sharing a key/value head meet in the same L2.
+// Otherwise a run would end inside a head, and with a causal diagonal the XCD holding a head's
+// heavy tiles would work far longer than the one holding its light tiles: the logical order is
+// then dealt out round-robin (logical index = hardware index), which gives every XCD every
+// eighth tile of each head.
 __device__ __forceinline__ TileRef map_tile(const KParams& p, int64_t tile_rows) {
   const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = (int64_t)blockIdx.x;
-  const int64_t x = bid & 7, k = bid >> 3;
-  const int64_t q = nblk >> 3, rem = nblk & 7;
-  const int64_t logical = x * q + (x < rem ? x : rem) + k;
+  int64_t logical = bid;
+  if ((((int64_t)p.B * p.Hq) & 7) == 0) {
+    const int64_t x = bid & 7, k = bid >> 3;
+    const int64_t q = nblk >> 3, rem = nblk & 7;
+    logical = x * q + (x < rem ? x : rem) + k;
+  }
   const int64_t head = logical / p.tiles_per_head;
   int64_t t = logical - head * p.tiles_per_head;
   TileRef r;
