@@ -64,6 +64,7 @@ CASES = [
     (2, 256, 3, 3, 64, 4, "zigzag", "bf16"),
     (1, 80, 2, 2, 64, 2, "contiguous", "f32"),
     (1, 80, 2, 1, 128, 2, "zigzag", "f32"),
+    (1, 48, 2, 1, 64, 4, "zigzag", "f32"),  # fp32 forward with two running states
 ]
 
 
@@ -121,6 +122,7 @@ SPLIT_CASES = [
     (1, 64, 2, 1, 64, 1, "contiguous", "bf16"),
     (1, 80, 2, 2, 64, 2, "contiguous", "f32"),
     (1, 80, 2, 1, 128, 2, "zigzag", "f32"),
+    (1, 48, 2, 1, 64, 4, "zigzag", "f32"),  # fp32 forward with two running states
 ]
 
 
