@@ -174,20 +174,35 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(const void* __rest
   const int sub = (int)(t & 15);
   float acc = 0.f;
   if (row < nrows) {
-    const int per = D / 16;  // 4 or 8 elements
+    // D / 16 = 4 or 8 elements per lane, read as one or two 16-byte vectors (8 bytes for bf16
+    // at D = 64); the tensors are 16-byte aligned and rows are D elements.
+    const int per = D / 16;
     const long long base = row * D + sub * per;
     if (BF16) {
-      const u16* a = reinterpret_cast<const u16*>(o) + base;
-      const u16* b = reinterpret_cast<const u16*>(dO) + base;
-      for (int e = 0; e < per; ++e) {
-        const float x = __builtin_bit_cast(float, (unsigned)a[e] << 16);
-        const float y = __builtin_bit_cast(float, (unsigned)b[e] << 16);
-        acc = fmaf(x, y, acc);
+      // bf16 widens to fp32 exactly: the high half of a 32-bit word as is, the low one shifted
+      const unsigned* a = reinterpret_cast<const unsigned*>(reinterpret_cast<const u16*>(o) + base);
+      const unsigned* b = reinterpret_cast<const unsigned*>(reinterpret_cast<const u16*>(dO) + base);
+      auto dot2 = [&](unsigned x, unsigned y) {
+        acc = fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, x & 0xFFFF0000u), __builtin_bit_cast(float, y & 0xFFFF0000u), acc);
+      };
+      if (per == 8) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a), y = *reinterpret_cast<const u32x4*>(b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot2(x[e], y[e]);
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(a), y = *reinterpret_cast<const u32x2*>(b);
+        dot2(x[0], y[0]);
+        dot2(x[1], y[1]);
       }
     } else {
-      const float* a = reinterpret_cast<const float*>(o) + base;
-      const float* b = reinterpret_cast<const float*>(dO) + base;
-      for (int e = 0; e < per; ++e) acc = fmaf(a[e], b[e], acc);
+      const f32x4* a = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(o) + base);
+      const f32x4* b = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(dO) + base);
+      for (int v = 0; v < per / 4; ++v) {
+        const f32x4 x = a[v], y = b[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(x[e], y[e], acc);
+      }
     }
   }
 #pragma unroll

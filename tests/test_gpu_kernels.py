@@ -117,16 +117,17 @@ def test_lse_merge_matches_oracle(ctx):
     assert np.max(np.abs(to_f64(Ud) - rU)) < 1e-5
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_preprocess_and_cast(ctx, dtype):
-    prob = api.Problem(2, 80, 3, 3, 128, 1, "contiguous", dtype)
-    o = to_dev(rand_store((2, 3, 80, 128), dtype, 21), dtype)
-    do = to_dev(rand_store((2, 3, 80, 128), dtype, 22), dtype)
+def test_preprocess_and_cast(ctx, dtype, D):
+    prob = api.Problem(2, 80, 3, 3, D, 1, "contiguous", dtype)
+    o = to_dev(rand_store((2, 3, 80, D), dtype, 21), dtype)
+    do = to_dev(rand_store((2, 3, 80, D), dtype, 22), dtype)
     delta = api.ra_bwd_preprocess(ctx, prob, o, do)
     torch.cuda.synchronize()
     ref = np.sum(to_f64(o) * to_f64(do), axis=-1)
     assert np.max(np.abs(to_f64(delta) - ref)) < 1e-4
-    src = torch.randn(2, 3, 80, 128, device="cuda") * 5
+    src = torch.randn(2, 3, 80, D, device="cuda") * 5
     out = api.ra_cast_from_f32(ctx, prob, src)
     torch.cuda.synchronize()
     if dtype == "bf16":
