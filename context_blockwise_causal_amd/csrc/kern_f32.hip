@@ -36,10 +36,16 @@ __global__ __launch_bounds__(64) void chunk_fwd_f32_kernel(const KParams p) {
   for (int d = lane; d < D; d += 64) qs[d] = Q[qrow * D + d];
   __syncthreads();
 
-  float m = p.m[qrow], l = p.l[qrow];
+  float m = -__builtin_inff(), l = 0.f;
   float o[PER];
 #pragma unroll
-  for (int t = 0; t < PER; ++t) o[t] = p.U[qrow * D + lane + 64 * t];
+  for (int t = 0; t < PER; ++t) o[t] = 0.f;
+  if (!p.fresh) {
+    m = p.m[qrow];
+    l = p.l[qrow];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) o[t] = p.U[qrow * D + lane + 64 * t];
+  }
 
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {

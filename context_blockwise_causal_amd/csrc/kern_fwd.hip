@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
   float m2 = -__builtin_inff(), lsum = 0.f;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-  if (qvalid) {
+  if (qvalid && !p.fresh) {
     m2 = p.m[qrow] * kLog2e;
     lsum = p.l[qrow];
 #pragma unroll

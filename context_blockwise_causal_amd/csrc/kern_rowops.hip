@@ -138,6 +138,39 @@ __device__ __forceinline__ u16 f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(u16, (__bf16)f);
 }
 
+// Two running states of the same rows (from steps that ran on different streams) merged and
+// finalized in one pass: the merge of state_merge_kernel followed by the division and the LSE
+// of finalize_kernel, without writing the merged state back.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void merge_finalize_kernel(const f32x4* __restrict__ Ub,
+                                                                  const float* __restrict__ mb,
+                                                                  const float* __restrict__ lb,
+                                                                  const f32x4* __restrict__ Ua,
+                                                                  const float* __restrict__ ma,
+                                                                  const float* __restrict__ la,
+                                                                  void* __restrict__ o,
+                                                                  float* __restrict__ lse,
+                                                                  long long nrows, int vec_shift) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (nrows << vec_shift)) return;
+  const long long row = i >> vec_shift;
+  const float mo = ma[row], mq = mb[row];
+  const float mn = fmaxf(mo, mq);
+  const float a = rescale(mo, mn), b = rescale(mq, mn);
+  const f32x4 u = a * Ua[i] + b * Ub[i];
+  const float lr = a * la[row] + b * lb[row];
+  const float inv = lr > 0.f ? 1.0f / lr : 0.f;
+  const f32x4 v = u * inv;
+  if (BF16) {
+    const unsigned lo = (unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+    const unsigned hi = (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+    reinterpret_cast<uint2*>(o)[i] = make_uint2(lo, hi);
+  } else {
+    reinterpret_cast<f32x4*>(o)[i] = v;
+  }
+  if ((i & ((1ll << vec_shift) - 1)) == 0) lse[row] = lr > 0.f ? mn + logf(lr) : -__builtin_inff();
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const f32x4* __restrict__ U,
                                                             const float* __restrict__ m,
@@ -322,6 +355,21 @@ int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U,
   else
     hipLaunchKernelGGL(finalize_kernel<false>, dim3(blocks_for(n)), dim3(kThreads), 0,
                        (hipStream_t)stream, (const f32x4*)U, m, l, o, lse, (long long)nrows, vs);
+  return (int)hipGetLastError();
+}
+
+int launch_merge_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* Ub, const float* mb,
+                          const float* lb, const float* Ua, const float* ma, const float* la, void* o,
+                          float* lse, void* stream) {
+  const int vs = log2i(D / 4);
+  const long long n = (long long)nrows << vs;
+  if (n == 0) return 0;
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(merge_finalize_kernel<true>, dim3(blocks_for(n)), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const f32x4*)Ub, mb, lb, (const f32x4*)Ua, ma, la, o, lse, (long long)nrows, vs);
+  else
+    hipLaunchKernelGGL(merge_finalize_kernel<false>, dim3(blocks_for(n)), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const f32x4*)Ub, mb, lb, (const f32x4*)Ua, ma, la, o, lse, (long long)nrows, vs);
   return (int)hipGetLastError();
 }
 

@@ -451,16 +451,22 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   float* U2 = reinterpret_cast<float*>(ws + W.U2);
   float* m2 = reinterpret_cast<float*>(ws + W.m2);
   float* l2 = reinterpret_cast<float*>(ws + W.l2);
-  if ((e = launch_state_init(rows, s.D, U, m, l, cs))) return dev_err(e, "state init");
+  // The first step (the local one, which the ring loop runs first) has pairs covering every row
+  // of the slice (its diagonal pairs are never skipped), so it starts from the empty state
+  // instead of reading an initialised one.  The second state is initialised: its steps may
+  // leave rows untouched.
   if (two && (e = launch_state_init(rows, s.D, U2, m2, l2, cs))) return dev_err(e, "state init");
   KParams kp = base_params(s);
   kp.q = q_slice;
   kp.q_head_rows = s.chunk;
+  bool first = true;
   auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     (void)owner;
     const bool b = t != cs;  // slot-1 steps run on the second stream
     kp.U = b ? U2 : U; kp.m = b ? m2 : m; kp.l = b ? l2 : l;
+    kp.fresh = first ? 1 : 0;
+    first = false;
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
     kp.dkv_head_rows = kv_head_rows;
@@ -469,7 +475,9 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr,
                       two ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
-  if (two && (e = launch_state_merge(rows, s.D, U2, m2, l2, U, m, l, cs))) return dev_err(e, "state merge");
+  if (two)
+    return dev_err(launch_merge_finalize(rows, s.D, s.dtype, U2, m2, l2, U, m, l, o_slice, lse_slice, cs),
+                   "forward merge and finalize");
   return dev_err(launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, cs),
                  "forward finalize");
 }

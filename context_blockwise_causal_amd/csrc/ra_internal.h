@@ -92,6 +92,7 @@ struct KParams {
   float scale_log2;       // scale * log2(e)
   int64_t window;         // sliding window (0 = none)
   int64_t attn_chunk;     // attention chunk (0 = none)
+  int32_t fresh;          // forward: start every row from the empty state instead of loading U, m, l
   int32_t nranges;
   int64_t tiles_per_head;
   KRange ranges[4];
@@ -156,6 +157,11 @@ int launch_state_merge(int64_t nrows, int64_t D, const float* Up, const float* m
                        float* U, float* m, float* l, void* stream);
 int launch_fwd_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* U, const float* m,
                         const float* l, void* o, float* lse, void* stream);
+// launch_state_merge of (Ub, mb, lb) into (Ua, ma, la) followed by launch_fwd_finalize, in one
+// pass that does not write the merged state.
+int launch_merge_finalize(int64_t nrows, int64_t D, int32_t dtype, const float* Ub, const float* mb,
+                          const float* lb, const float* Ua, const float* ma, const float* la, void* o,
+                          float* lse, void* stream);
 int launch_bwd_preprocess(int64_t nrows, int64_t D, int32_t dtype, const void* o,
                           const void* dO, float* delta, void* stream);
 int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, void* stream);
