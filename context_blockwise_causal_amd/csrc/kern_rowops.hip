@@ -264,6 +264,35 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(f32x4* __restrict__
     dst[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Zeroes blocks x nvec 16-byte vectors spaced pitch_vec apart; grid.y walks the blocks.
+__global__ __launch_bounds__(kThreads) void zero2d_kernel(u32x4* __restrict__ dst, long long pitch_vec,
+                                                          long long nvec) {
+  const long long b = blockIdx.y;
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+    dst[b * pitch_vec + i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Casts blocks x nvec groups of 4 fp32 values to the output dtype; source and destination
+// blocks are pitch4 groups of 4 elements apart.  grid.y walks the blocks.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void cast2d_kernel(const f32x4* __restrict__ src, void* __restrict__ dst,
+                                                          long long pitch4, long long nvec) {
+  const long long b = blockIdx.y;
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const long long j = b * pitch4 + i;
+    const f32x4 v = src[j];
+    if (BF16) {
+      const unsigned lo = (unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+      const unsigned hi = (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+      reinterpret_cast<uint2*>(dst)[j] = make_uint2(lo, hi);
+    } else {
+      reinterpret_cast<f32x4*>(dst)[j] = v;
+    }
+  }
+}
+
 // blocks x (block_bytes / 16) vectors; grid.y walks the blocks.
 __global__ __launch_bounds__(kThreads) void copy2d_kernel(const u32x4* __restrict__ src,
                                                           long long src_pitch_vec,
@@ -395,6 +424,35 @@ int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, 
   else
     hipLaunchKernelGGL(cast_kernel<false>, dim3(blocks_for(nvec)), dim3(kThreads), 0,
                        (hipStream_t)stream, (const f32x4*)src, dst, nvec);
+  return (int)hipGetLastError();
+}
+
+// Grid width for a blocks x nvec 2-D pass: enough workgroups to fill the chip in total.
+inline long long grid2d_x(long long nvec, long long blocks) {
+  long long gx = (nvec + kThreads - 1) / kThreads;
+  const long long cap = blocks >= 2048 ? 1 : 2048 / blocks;
+  return gx > cap ? cap : gx;
+}
+
+int launch_zero2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t blocks, void* stream) {
+  const long long nvec = block_bytes / 16;
+  if (nvec == 0 || blocks == 0) return 0;
+  hipLaunchKernelGGL(zero2d_kernel, dim3((unsigned)grid2d_x(nvec, blocks), (unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (u32x4*)dst, (long long)(pitch_bytes / 16), nvec);
+  return (int)hipGetLastError();
+}
+
+int launch_cast2d(const float* src, void* dst, int64_t pitch, int64_t block, int64_t blocks, int32_t dtype,
+                  void* stream) {
+  const long long nvec = block / 4;
+  if (nvec == 0 || blocks == 0) return 0;
+  const dim3 grid((unsigned)grid2d_x(nvec, blocks), (unsigned)blocks);
+  if (dtype == RA_BF16)
+    hipLaunchKernelGGL(cast2d_kernel<true>, grid, dim3(kThreads), 0, (hipStream_t)stream, (const f32x4*)src, dst,
+                       (long long)(pitch / 4), nvec);
+  else
+    hipLaunchKernelGGL(cast2d_kernel<false>, grid, dim3(kThreads), 0, (hipStream_t)stream, (const f32x4*)src, dst,
+                       (long long)(pitch / 4), nvec);
   return (int)hipGetLastError();
 }
 

@@ -575,10 +575,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   DeviceGuard g(ctx->device);
   int e;
   const int64_t rows = s.B * s.Hq * s.chunk;
-  const int64_t kvel = s.B * s.Hkv * s.S * s.D;
   if ((e = launch_fill_zero(rows * s.D, dq, cs))) return dev_err(e, "zero dq");
-  if ((e = launch_fill_zero(kvel, dk, cs))) return dev_err(e, "zero dk");
-  if ((e = launch_fill_zero(kvel, dv, cs))) return dev_err(e, "zero dv");
   if ((e = launch_bwd_preprocess(rows, s.D, s.dtype, o_slice, dO_slice, delta, cs)))
     return dev_err(e, "backward preprocess");
   KParams kp = base_params(s);
@@ -592,14 +589,30 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   // slot 1 run theirs on a second pool stream, beside those of the compute stream.
   hipStream_t side = ctx->pool[0];
   const BwdFork fork{side, ctx->bfork, nullptr};
+  // Each owner's chunk is the K/V of exactly one ring step, so its dK/dV rows are complete once
+  // that step's dK/dV kernel has run (the dQ kernels do not touch them): the rows are zeroed
+  // just before it and cast into dk_ring / dv_ring just after it, on the same stream -- the
+  // ring's return of the K/V gradients to their owner, overlapping the later steps.
+  const int64_t blk = s.chunk * s.D;  // one owner's rows of one (batch, kv head)
+  const int64_t pitch = s.S * s.D;    // head stride of the ring-ordered tensors
+  const int64_t nkvh = s.B * s.Hkv;
+  bool visited[64] = {};
   auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
                   const ra_pair* pairs, int32_t n) -> int {
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
-    // gradients of owner o's chunk go to its rows of the ring-ordered accumulators
-    kp.dk = dk + (int64_t)owner * s.chunk * s.D;
-    kp.dv = dv + (int64_t)owner * s.chunk * s.D;
-    return run_bwd(s, kp, pairs, n, t, &fork);
+    float* const dko = dk + (int64_t)owner * blk;
+    float* const dvo = dv + (int64_t)owner * blk;
+    int r;
+    if ((r = launch_zero2d(dko, pitch * 4, blk * 4, nkvh, t))) return r;
+    if ((r = launch_zero2d(dvo, pitch * 4, blk * 4, nkvh, t))) return r;
+    kp.dk = dko;
+    kp.dv = dvo;
+    if ((r = run_bwd(s, kp, pairs, n, t, &fork))) return r;
+    visited[owner] = true;
+    const int64_t off = (int64_t)owner * blk * s.esize;
+    if ((r = launch_cast2d(dko, static_cast<char*>(dk_ring) + off, pitch, blk, nkvh, s.dtype, t))) return r;
+    return launch_cast2d(dvo, static_cast<char*>(dv_ring) + off, pitch, blk, nkvh, s.dtype, t);
   };
   // (the fp32 path adds dQ inside its single kernel: its steps stay on one stream)
   if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side,
@@ -608,8 +621,15 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   if ((e = (int)hipEventRecord(ctx->bjoin, side))) return dev_err(e, "record dq join");
   if ((e = (int)hipStreamWaitEvent(cs, ctx->bjoin, 0))) return dev_err(e, "wait dq join");
   if ((e = launch_cast_from_f32(rows * s.D, s.dtype, dq, dq_slice, cs))) return dev_err(e, "cast dq");
-  if ((e = launch_cast_from_f32(kvel, s.dtype, dk, dk_ring, cs))) return dev_err(e, "cast dk");
-  if ((e = launch_cast_from_f32(kvel, s.dtype, dv, dv_ring, cs))) return dev_err(e, "cast dv");
+  // owners whose chunk no step attends to (skipped steps) get zero gradients
+  for (int32_t o = 0; o < s.cp; ++o) {
+    if (visited[o]) continue;
+    const int64_t off = (int64_t)o * blk * s.esize;
+    if ((e = launch_zero2d(static_cast<char*>(dk_ring) + off, pitch * s.esize, blk * s.esize, nkvh, cs)))
+      return dev_err(e, "zero dk");
+    if ((e = launch_zero2d(static_cast<char*>(dv_ring) + off, pitch * s.esize, blk * s.esize, nkvh, cs)))
+      return dev_err(e, "zero dv");
+  }
   return RA_OK;
 }
 

@@ -166,6 +166,12 @@ int launch_bwd_preprocess(int64_t nrows, int64_t D, int32_t dtype, const void* o
                           const void* dO, float* delta, void* stream);
 int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, void* stream);
 int launch_fill_zero(int64_t n_floats, float* dst, void* stream);
+// `blocks` blocks of block_bytes (a multiple of 16) zeroed, pitch_bytes apart.
+int launch_zero2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t blocks, void* stream);
+// `blocks` blocks of `block` fp32 values (a multiple of 4) cast to dtype; source and destination
+// blocks start `pitch` elements apart.
+int launch_cast2d(const float* src, void* dst, int64_t pitch, int64_t block, int64_t blocks, int32_t dtype,
+                  void* stream);
 // Copies `blocks` blocks of `block_bytes` from src (pitch src_pitch) to dst (pitch dst_pitch).
 int launch_copy2d(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch,
                   int64_t block_bytes, int64_t blocks, void* stream);
