@@ -271,9 +271,10 @@ ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* problem, int
  * over all ranks gives the full-sequence gradient -- the ring's return-to-owner.
  * Staging and slot reuse as for the forward.  In the bf16 path each step's dQ kernel runs on a
  * context stream (in step order: the steps add into the same dQ rows) and the dK/dV kernels of
- * the steps staged in slot 1 on a second one (steps write different owners' rows); both are
- * joined into `compute` before the final casts, so all work is ordered before later work on
- * `compute`.  dK/dV sums over the query heads of a group use fp32 atomics, whose order (and so
+ * the steps staged in slot 1 on a second one (steps write different owners' rows).  An owner's
+ * rows of dk_ring / dv_ring are written right after its step, on that step's stream; both
+ * context streams are joined into `compute` before the dQ cast, so all work is ordered before
+ * later work on `compute`.  dK/dV sums over the query heads of a group use fp32 atomics, whose order (and so
  * the last bits of dk_ring, dv_ring) can vary from run to run.
  * Workspace: ra_workspace_size(problem, 1). */
 ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* problem, int32_t rank,
