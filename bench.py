@@ -184,15 +184,19 @@ def kernel_rates(api, ctx, prob, wl, bufs, launches, stream, backward, reps=3):
     return out
 
 
+# The files the chunk kernels' code and parameter block come from: the stored counter readings
+# describe these kernels and stay valid while these files do.
+CHUNK_KERNEL_SOURCES = ("kern_bwd.hip", "kern_common.h", "kern_fwd.hip", "ra_internal.h")
+
+
 def source_hash():
-    """Hash of the kernel sources: stored counter readings are used only while it matches."""
+    """Hash of the chunk kernels' sources: stored counter readings are used only while it matches."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "context_blockwise_causal_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in CHUNK_KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
