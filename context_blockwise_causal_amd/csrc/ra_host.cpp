@@ -36,6 +36,24 @@ struct ra_context {
 namespace ra {
 namespace {
 
+// Orders `side` before `main` (record on side, wait on main) when it goes out of scope while
+// armed: every return path of a driver that forked work onto a context stream joins it, so
+// that even after an error all enqueued work is ordered before later work on the caller's
+// stream.  The success path joins explicitly (reporting errors) and disarms it.
+struct JoinGuard {
+  hipEvent_t ev;
+  hipStream_t side, main;
+  bool armed;
+  void join_now() {
+    if (armed) {
+      (void)hipEventRecord(ev, side);
+      (void)hipStreamWaitEvent(main, ev, 0);
+    }
+    armed = false;
+  }
+  ~JoinGuard() { join_now(); }
+};
+
 struct DeviceGuard {
   int prev = -1;
   bool ok = false;
@@ -178,6 +196,7 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   ra_status st;
   const bool use_alt = alt && alt != cs && nstaged > 1;
   hipStream_t kvs[2] = {cs, use_alt ? alt : cs};
+  JoinGuard alt_join{ctx->ajoin, alt, cs, use_alt};
   if ((nstaged > 0 && ss != cs) || use_alt) {
     // The slots may still be read by earlier work on the compute stream, and the second compute
     // stream starts after everything the caller queued before the loop.
@@ -204,10 +223,38 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
     if (side && (e = (int)hipEventRecord(ctx->qfreed[sl], side))) return dev_err(e, "record slot_free (side)");
   }
   if (use_alt) {
+    alt_join.armed = false;
     if ((e = (int)hipEventRecord(ctx->ajoin, alt))) return dev_err(e, "record alt join");
     if ((e = (int)hipStreamWaitEvent(cs, ctx->ajoin, 0))) return dev_err(e, "wait alt join");
   }
   return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+namespace ra {
+namespace {
+
+// Destroys the context's events and streams that exist (all of them after a successful
+// ra_create, those created so far after a failed one; the rest are null), then the context.
+// The caller has made the context's device current.
+void release(ra_context* c) {
+  auto ev = [](hipEvent_t x) { if (x) (void)hipEventDestroy(x); };
+  ev(c->start);
+  for (int i = 0; i < 2; ++i) {
+    ev(c->ready[i]);
+    ev(c->freed[i]);
+    ev(c->qfreed[i]);
+  }
+  ev(c->ajoin);
+  for (int i = 0; i < kMaxSteps; ++i) ev(c->done[i]);
+  ev(c->fin);
+  ev(c->bfork);
+  ev(c->bjoin);
+  for (int i = 0; i < kPoolStreams; ++i)
+    if (c->pool[i]) (void)hipStreamDestroy(c->pool[i]);
+  delete c;
 }
 
 }  // namespace
@@ -243,7 +290,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
   for (int i = 0; i < kPoolStreams && e == hipSuccess; ++i)
     e = hipStreamCreateWithFlags(&c->pool[i], hipStreamNonBlocking);
   if (e != hipSuccess) {
-    delete c;
+    release(c);  // the handles created before the failure
     return fail(RA_ERR_DEVICE, "event or stream creation failed: %s", hipGetErrorString(e));
   }
   *out = c;
@@ -253,19 +300,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
 void ra_destroy(ra_context* c) {
   if (!c) return;
   DeviceGuard g(c->device);
-  (void)hipEventDestroy(c->start);
-  for (int i = 0; i < 2; ++i) {
-    (void)hipEventDestroy(c->ready[i]);
-    (void)hipEventDestroy(c->freed[i]);
-    (void)hipEventDestroy(c->qfreed[i]);
-  }
-  (void)hipEventDestroy(c->ajoin);
-  for (int i = 0; i < kMaxSteps; ++i) (void)hipEventDestroy(c->done[i]);
-  (void)hipEventDestroy(c->fin);
-  (void)hipEventDestroy(c->bfork);
-  (void)hipEventDestroy(c->bjoin);
-  for (int i = 0; i < kPoolStreams; ++i) (void)hipStreamDestroy(c->pool[i]);
-  delete c;
+  release(c);
 }
 
 ra_status ra_layout_gather(ra_context* ctx, const ra_problem* prob, int32_t rank_begin,
@@ -511,6 +546,11 @@ ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* prob, int32_
   for (int i = 0; i < kPoolStreams; ++i)
     if ((e = (int)hipStreamWaitEvent(ctx->pool[i], ctx->start, 0))) return dev_err(e, "pool wait start");
   if (ms != cs && (e = (int)hipStreamWaitEvent(ms, ctx->start, 0))) return dev_err(e, "merge wait start");
+  // on an error return, the pool streams and the merge stream are still joined into `compute`
+  JoinGuard pool_join[kPoolStreams] = {};
+  for (int i = 0; i < kPoolStreams; ++i) pool_join[i] = JoinGuard{ctx->ajoin, ctx->pool[i], cs, false};
+  for (int i = 0; i < kPoolStreams; ++i) pool_join[i].armed = true;
+  JoinGuard merge_join{ctx->fin, ms, cs, ms != cs};
   if ((e = launch_state_init(rows, s.D, U, m, l, ms))) return dev_err(e, "state init");
   int np = 0;
   for (int32_t i = 0; i < s.cp; ++i) {
@@ -541,6 +581,9 @@ ra_status ra_rank_view_fwd_split(ra_context* ctx, const ra_problem* prob, int32_
   }
   if ((e = launch_fwd_finalize(rows, s.D, s.dtype, U, m, l, o_slice, lse_slice, ms)))
     return dev_err(e, "forward finalize");
+  // every pool stream's work is ordered before the merge stream's (done events)
+  for (int i = 0; i < kPoolStreams; ++i) pool_join[i].armed = false;
+  merge_join.armed = false;
   if (ms != cs) {
     if ((e = (int)hipEventRecord(ctx->fin, ms))) return dev_err(e, "record fin");
     if ((e = (int)hipStreamWaitEvent(cs, ctx->fin, 0))) return dev_err(e, "compute wait fin");
@@ -589,6 +632,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   // slot 1 run theirs on a second pool stream, beside those of the compute stream.
   hipStream_t side = ctx->pool[0];
   const BwdFork fork{side, ctx->bfork, nullptr};
+  JoinGuard side_join{ctx->bjoin, side, cs, true};
   // Each owner's chunk is the K/V of exactly one ring step, so its dK/dV rows are complete once
   // that step's dK/dV kernel has run (the dQ kernels do not touch them): the rows are zeroed
   // just before it and cast into dk_ring / dv_ring just after it, on the same stream -- the
@@ -618,6 +662,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side,
                       s.dtype == RA_BF16 ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
+  side_join.armed = false;
   if ((e = (int)hipEventRecord(ctx->bjoin, side))) return dev_err(e, "record dq join");
   if ((e = (int)hipStreamWaitEvent(cs, ctx->bjoin, 0))) return dev_err(e, "wait dq join");
   if ((e = launch_cast_from_f32(rows * s.D, s.dtype, dq, dq_slice, cs))) return dev_err(e, "cast dq");
