@@ -92,6 +92,29 @@ def test_delayed_staging_gives_identical_forward(ctx):
     assert np.array_equal(bits(o), bits(o_ref)) and np.array_equal(bits(lse), bits(lse_ref))
 
 
+def test_backward_dq_does_not_depend_on_timing(ctx):
+    """The backward's dQ kernels add in ring-step order on one stream, so dQ is bit-identical
+    when the staging stream is held back; dK/dV sum query heads with atomics in any order and
+    agree to fp32 rounding."""
+    prob, t, dev, k_ring, v_ring = setup(ctx, 1, 8 * 256, 4, 2, 128, 8, "zigzag", "bf16", 78)
+    rank = 5
+    q_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["q"])
+    do_sl = api.ra_layout_gather(ctx, prob, rank, 1, dev["do"])
+    o, lse = api.rank_view_fwd(ctx, prob, rank, q_sl, k_ring, v_ring)
+    ref = api.rank_view_bwd(ctx, prob, rank, q_sl, k_ring, v_ring, o, lse, do_sl)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big * 1e-3  # keeps the staging stream busy before the copies start
+    got = api.rank_view_bwd(ctx, prob, rank, q_sl, k_ring, v_ring, o, lse, do_sl, staging=side)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got[0]), bits(ref[0]))
+    for g, r in zip(got[1:], ref[1:]):
+        assert np.max(np.abs(to_f64(g) - to_f64(r))) <= 1e-2 * max(1.0, np.max(np.abs(to_f64(r))))
+
+
 def test_workspace_too_small_enqueues_nothing(ctx):
     prob, t, dev, k_ring, v_ring = setup(ctx, 1, 512, 2, 2, 64, 2, "contiguous", "bf16", 5)
     q_sl = api.ra_layout_gather(ctx, prob, 0, 1, dev["q"])
