@@ -65,6 +65,10 @@ CASES = [
     (1, 80, 2, 2, 64, 2, "contiguous", "f32"),
     (1, 80, 2, 1, 128, 2, "zigzag", "f32"),
     (1, 48, 2, 1, 64, 4, "zigzag", "f32"),  # fp32 forward with two running states
+    # odd numbers of staged steps and slot-pair reuse across groups of staged steps
+    (1, 64, 2, 1, 64, 3, "zigzag", "bf16"),
+    (1, 64, 2, 2, 64, 8, "contiguous", "bf16"),
+    (1, 64, 4, 1, 128, 8, "zigzag", "bf16"),
 ]
 
 
@@ -146,6 +150,10 @@ SPLIT_CASES = [
     (1, 80, 2, 2, 64, 2, "contiguous", "f32"),
     (1, 80, 2, 1, 128, 2, "zigzag", "f32"),
     (1, 48, 2, 1, 64, 4, "zigzag", "f32"),  # fp32 forward with two running states
+    # odd numbers of staged steps and slot-pair reuse across groups of staged steps
+    (1, 64, 2, 1, 64, 3, "zigzag", "bf16"),
+    (1, 64, 2, 2, 64, 8, "contiguous", "bf16"),
+    (1, 64, 4, 1, 128, 8, "zigzag", "bf16"),
 ]
 
 
