@@ -12,8 +12,9 @@ What it computes, and from which passage of the pages:
   softmax and safe-softmax equations and the per-step partial-attention equation; the
   InfiniTrain pull request "Feat: Context Parallel" review thread that spells the chain
   q@k^T * 1/sqrt(D) -> MaskedFill -> Softmax -> @v.
-* Causal visibility: a query at global position t sees the keys at positions j <= t
-  ("Zig-Zag Ring Attention" section: token i only sees [1, i]).
+* Causal visibility: a query at global position t sees the keys at positions j <= t, itself
+  included (lecture note "上下文并行", section "Zig-Zag Ring Attention", the statement of which
+  tokens each token attends to).
 * GQA: query head h reads key/value head h // n_rep, n_rep = Hq / Hkv.  This is the grouping
   that the RepeatKVHeads gradient reshape (B, H/n_rep, n_rep, T, D).Sum(2) implies
   ("Feat: Context Parallel", review thread on the attention helper).
@@ -156,8 +157,8 @@ def _key_limit(k_pos: np.ndarray, k_sorted: bool, qmax: int) -> int:
 def visible(q_pos, k_pos, window: int = 0, attn_chunk: int = 0):
     """Visibility matrix (len(q_pos), len(k_pos)) of the causal mask and its two restrictions.
 
-    Causal: key j is visible to query t iff j <= t ("Zig-Zag Ring Attention": token i sees
-    [1, i]).  The transformers context-parallel page names two further masks the attention
+    Causal: key j is visible to query t iff j <= t, the diagonal included ("Zig-Zag Ring
+    Attention" section of the lecture note).  The transformers context-parallel page names two further masks the attention
     call must rebuild over the whole sequence, sliding-window and chunked attention; read as
     the usual definitions: with a window W > 0 the query also needs t - j < W (itself and the
     W - 1 keys before it), with an attention chunk C > 0 it needs j // C == t // C (keys of its
@@ -265,6 +266,37 @@ def attention_rows_bwd(q, k, v, do, q_pos, k_pos, scale=None, window: int = 0, a
                 dk[b, g, :kn] += sc * (ds.T @ qb)
                 dv[b, g, :kn] += p.T @ dob
     return dq, dk, dv
+
+
+def key_grads(q, k, v, do, q_pos, k_pos, o, lse, scale=None, window: int = 0, attn_chunk: int = 0):
+    """dK and dV of the keys at ``k_pos`` from the query rows at ``q_pos``, given those rows'
+    output O and LSE over their whole visible key set (from ``attention_rows``).
+
+    The same gradient as ``attention_rows_bwd`` restricted to a subset of keys: a key's gradient
+    needs, besides its own scores, only the row statistics LSE_t and D_t = <dO_t, O_t>, so the
+    rows' keys outside the subset enter through O and LSE alone.  Per row t and key j:
+      P_tj = exp(s_tj - LSE_t),  dS_tj = P_tj (<dO_t, v_j> - D_t),
+      dk_j = scale sum_t dS_tj q_t,  dv_j = sum_t P_tj dO_t  (summed over the query heads
+    that read the key's head).  q, do, o: (B, Hq, T, D); lse: (B, Hq, T); k, v: the subset's
+    keys and values (B, Hkv, Tk, D).  Returns dk, dv (B, Hkv, Tk, D).
+    """
+    q, k, v, do, o, lse = (np.asarray(a, np.float64) for a in (q, k, v, do, o, lse))
+    B, Hq, T, D = q.shape
+    n_rep = Hq // k.shape[1]
+    sc = _scale(D, scale)
+    delta = np.sum(do * o, axis=-1)
+    vis = visible(q_pos, k_pos, window, attn_chunk)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // n_rep
+            lb = np.where(np.isfinite(lse[b, h]), lse[b, h], 0.0)
+            p = np.where(vis, np.exp(sc * (q[b, h] @ k[b, g].T) - lb[:, None]), 0.0)
+            ds = p * (do[b, h] @ v[b, g].T - delta[b, h][:, None])
+            dk[b, g] += sc * (ds.T @ q[b, h])
+            dv[b, g] += p.T @ do[b, h]
+    return dk, dv
 
 
 # ----------------------------------------------------------------------------- rank views

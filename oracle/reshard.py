@@ -16,10 +16,21 @@ sequence sharding.  Written here as the definition:
 * the pack / unpack steps on either side of it, each a slicing or concatenation.
 
 Tensors are (B, H, S, D); send / receive buffers are (cp, B, H/cp, S/cp, D).
+
+The a2a+p2p composition ("Feat: Context Parallel", 主要改动, the mode table: an all-to-all
+layout change inside sub-groups, then ring attention; "上下文并行", section USP: all-to-all inside
+a node, ring across nodes) arranges A * R ranks as R ring groups of A members.  Reading taken
+where the pages leave the token assignment open: the ring layout (contiguous or zigzag over R)
+gives ring group g its tokens, in slice order, and member u of the group holds the u-th of A
+equal contiguous pieces of them (``usp_positions``).  The all-to-all inside a group leaves member
+u with all the group's tokens for heads [u H/A, (u+1) H/A); the ring then runs across the groups
+among the members that hold the same heads.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from oracle import attn64 as _attn
 
 
 def seq_shard(full, cp, r):
@@ -60,3 +71,11 @@ def exchange(send):
     """The all-to-all on a list of per-rank send buffers: recv[r][j] = send[j][r]."""
     cp = len(send)
     return [np.stack([send[j][r] for j in range(cp)]) for r in range(cp)]
+
+
+def usp_positions(seq_len, a2a, ring, layout, group, member):
+    """Sequence positions rank (group, member) holds before the all-to-all: the member-th of
+    ``a2a`` contiguous pieces of ring group ``group``'s slice (ring layout over ``ring``)."""
+    pos = _attn.rank_positions(seq_len, ring, layout, group)
+    n = len(pos) // a2a
+    return pos[member * n:(member + 1) * n]

@@ -406,3 +406,73 @@ def test_merge_of_empty_states_stays_empty():
     assert np.all(st[0] == 0) and np.all(np.isneginf(st[1])) and np.all(st[2] == 0)
     o, lse = O.finalize(st)
     assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def _pair_positions_pinned(fn) -> bool:
+    """True when ``fn(kind, q_len, kv_len)`` returns positions whose causal visibility matrix is
+    exactly the pair kind it was asked for ("上下文并行", Zig-Zag Ring Attention: causal means key
+    j is visible to query i iff j <= i).  The check computes the visibility matrix itself rather
+    than calling ``classify``, so that a mistake shared by the two functions would still show."""
+    for n, m in ((1, 1), (5, 5), (16, 16), (7, 3), (3, 9)):
+        kinds = [O.FULL, O.SKIP] + ([O.DIAG] if n == m else [])
+        for kind in kinds:
+            qp, kp = (np.asarray(a, np.int64) for a in fn(kind, n, m))
+            if qp.shape != (n,) or kp.shape != (m,):
+                return False
+            vis = np.array([[int(kp[j]) <= int(qp[i]) for j in range(m)] for i in range(n)])
+            want = {O.FULL: np.ones((n, m), bool), O.SKIP: np.zeros((n, m), bool),
+                    O.DIAG: np.tril(np.ones((n, m), bool))}[kind]
+            if not np.array_equal(vis, want):
+                return False
+            # a 1 x 1 diagonal pair is also a full one, which classify reports first
+            if O.classify(qp, kp) != (O.FULL if (kind == O.DIAG and n == 1) else kind):
+                return False
+    return True
+
+
+def test_pair_positions_realise_each_kind():
+    """pair_positions builds the position sets behind every single-pair GPU reference: each kind
+    must come out with exactly that visibility (brute force over tiny pairs)."""
+    assert _pair_positions_pinned(O.pair_positions)
+
+
+def test_pair_positions_pin_catches_planted_offsets():
+    """Planted mistakes in the positions (queries placed so the first one misses the last key for FULL, keys one
+    row too early for SKIP, a diagonal shifted by one) must fail the pin."""
+    def early_full(kind, n, m):
+        if kind == O.FULL:
+            return m - 2 + np.arange(n), np.arange(m)
+        return O.pair_positions(kind, n, m)
+
+    def early_skip(kind, n, m):
+        if kind == O.SKIP:
+            return np.arange(n), n - 1 + np.arange(m)
+        return O.pair_positions(kind, n, m)
+
+    def shifted_diag(kind, n, m):
+        if kind == O.DIAG:
+            return np.arange(n), 1 + np.arange(m)
+        return O.pair_positions(kind, n, m)
+
+    for bad in (early_full, early_skip, shifted_diag):
+        assert not _pair_positions_pinned(bad), bad.__name__
+
+
+@pytest.mark.parametrize("hq,hkv,window", [(4, 2, 0), (2, 2, 0), (3, 1, 5)])
+def test_key_grads_equal_full_backward_on_key_subsets(hq, hkv, window):
+    """key_grads (the gradient of a subset of keys from given row statistics) equals the pinned
+    full backward restricted to that subset, for scattered rows and keys."""
+    rng = np.random.default_rng(31)
+    S, D = 40, 8
+    q = rng.standard_normal((2, hq, S, D))
+    k = rng.standard_normal((2, hkv, S, D))
+    v = rng.standard_normal((2, hkv, S, D))
+    rows = np.sort(rng.choice(S, 17, replace=False))
+    do = rng.standard_normal((2, hq, len(rows), D))
+    kpos = np.arange(S)
+    _, rdk, rdv = O.attention_rows_bwd(q[:, :, rows], k, v, do, rows, kpos, window=window)
+    o, lse = O.attention_rows(q[:, :, rows], k, v, rows, kpos, window=window)
+    sel = np.sort(rng.choice(S, 11, replace=False))
+    dk, dv = O.key_grads(q[:, :, rows], k[:, :, sel], v[:, :, sel], do, rows, sel, o, lse, window=window)
+    assert np.max(np.abs(dk - rdk[:, :, sel])) < 1e-12
+    assert np.max(np.abs(dv - rdv[:, :, sel])) < 1e-12

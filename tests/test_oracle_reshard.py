@@ -4,6 +4,7 @@ sequence shards, the round trip is the identity, and a hand-checked tiny case.""
 import numpy as np
 import pytest
 
+from oracle import attn64 as O
 from oracle import reshard as R
 
 
@@ -52,3 +53,33 @@ def test_planted_mistake_is_caught():
     send = [R.pack_seq(R.seq_shard(x, 2, r), 2) for r in range(2)]
     wrong = [send[r] for r in range(2)]
     assert not np.array_equal(R.unpack_to_head(wrong[0]), R.head_shard(x, 2, 0))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("a2a,ring", [(1, 4), (2, 2), (2, 4), (4, 2), (3, 1)])
+def test_usp_positions_partition_and_reduce(layout, a2a, ring):
+    """The a2a+p2p token assignment: the A * R ranks' positions partition the sequence; each ring
+    group's members together hold exactly that group's ring slice, in slice order; A = 1 is the
+    ring layout itself and R = 1 the plain contiguous Ulysses split."""
+    S = 2 * a2a * ring * 6
+    allpos = np.concatenate([R.usp_positions(S, a2a, ring, layout, g, u)
+                             for g in range(ring) for u in range(a2a)])
+    assert np.array_equal(np.sort(allpos), np.arange(S))
+    for g in range(ring):
+        group = np.concatenate([R.usp_positions(S, a2a, ring, layout, g, u) for u in range(a2a)])
+        assert np.array_equal(group, O.rank_positions(S, ring, layout, g))
+    if a2a == 1:
+        for g in range(ring):
+            assert np.array_equal(R.usp_positions(S, 1, ring, layout, g, 0), O.rank_positions(S, ring, layout, g))
+    if ring == 1:
+        for u in range(a2a):
+            assert np.array_equal(R.usp_positions(S, a2a, 1, layout, 0, u),
+                                  np.arange(u * S // a2a, (u + 1) * S // a2a))
+
+
+def test_usp_positions_zigzag_example():
+    """By hand: 2 ring groups x 2 members, zigzag, 16 tokens (4 chunks of 4): group 0 holds chunks
+    0 and 3 = positions 0-3, 12-15, split between its members; group 1 chunks 1 and 2."""
+    want = {(0, 0): [0, 1, 2, 3], (0, 1): [12, 13, 14, 15], (1, 0): [4, 5, 6, 7], (1, 1): [8, 9, 10, 11]}
+    for (g, u), w in want.items():
+        assert list(R.usp_positions(16, 2, 2, "zigzag", g, u)) == w
