@@ -24,7 +24,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attention TFLOP/s fwd+bwd per rank view at 1 GPU; % of bf16 MFMA peak"
-DEFAULT_WORKLOAD = "llama-gqa-cp8-zigzag"
+DEFAULT_WORKLOAD = "long-ring-cp16-zigzag"
+# also timed (rank views only, fewer steps) and reported beside the headline
+EXTRA_WORKLOADS = ("long-ring-cp16-contiguous", "llama-gqa-cp8-zigzag")
 
 
 def visible_count(q_pos0, kv_pos0, q_len, kv_len, window, attn_chunk):
@@ -128,13 +130,15 @@ def chunk_launches(api, prob, wl, k_ring, v_ring):
     return out
 
 
-# Algorithmic FLOPs of each chunk kernel per unit of counted forward FLOPs: the forward does
-# Q K^T and P V; the dK/dV kernel S, dP, dV and dK; the dQ kernel S, dP and dQ.
-KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_kernel": 2.0, "chunk_bwd_q_kernel": 1.5}
+# Algorithmic FLOPs of each chunk kernel per unit of counted forward FLOPs (the metric's method
+# work): the forward does Q K^T and P V (1); the dK/dV kernel S, dP, dV and dK (2); the dQ kernel
+# of the rank views forms dQ from the stored dS (0.5).  Together: the backward's 2.5.
+KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_kernel": 2.0, "chunk_bwd_dq_ds_kernel": 0.5}
 
 
 def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
-    """One callable per chunk kernel, each launching exactly that kernel for a launch tuple."""
+    """One callable per chunk kernel, each launching exactly that kernel for a launch tuple: the
+    backward through ra_chunk_bwd_ds in its two phases (dK/dV storing dS, then dQ from it)."""
     import torch
     chunk = prob.chunk
     U, m, l = api.new_state(prob, chunk)
@@ -146,47 +150,57 @@ def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
         dq = torch.zeros((prob.batch, prob.heads_q, chunk, prob.head_dim), device="cuda")
         dk = torch.zeros((prob.batch, prob.heads_kv, chunk, prob.head_dim), device="cuda")
         dv = torch.zeros_like(dk)
+        nbytes = max(api.ra_chunk_bwd_ds_size(prob, chunk, chunk, L[1]) for L in launches)
+        scratch = torch.empty(max(16, nbytes), dtype=torch.uint8, device="cuda")
         b = lambda L: bufs[L[0]]
-        run["chunk_bwd_kv_kernel"] = lambda L: api.ra_chunk_bwd(
-            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], None, dk, dv, stream)
-        run["chunk_bwd_q_kernel"] = lambda L: api.ra_chunk_bwd(
-            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], dq, None, None, stream)
+        run["chunk_bwd_kv_kernel"] = lambda L: api.ra_chunk_bwd_ds(
+            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], None, dk, dv,
+            scratch, stream)
+        run["chunk_bwd_dq_ds_kernel"] = lambda L: api.ra_chunk_bwd_ds(
+            ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], dq, None, None,
+            scratch, stream)
     return run
 
 
 def kernel_rates(api, ctx, prob, wl, bufs, launches, stream, backward, reps=3):
     """Average launch duration of each chunk kernel over the workload's launches, timed with
-    HIP events on the launch stream, and its algorithmic rate."""
+    HIP events on the launch stream, and its algorithmic rate (method work, KERNEL_UNITS).
+    The dQ kernel reads the dS its launch's dK/dV phase stored, so the two backward phases are
+    replayed launch by launch, each phase bracketed by its own events."""
     import torch
     run = kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward)
-    out = {}
-    for name, fn in run.items():
-        for L in launches:
-            fn(L)
+    names = list(run)
+    times = {n: [0.0] * len(launches) for n in names}
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in launches] for n in names}
+    for rep in range(reps + 1):  # the first pass warms up
+        for j, L in enumerate(launches):
+            for n in names:
+                ev[n][j][0].record(stream)
+                run[n](L)
+                ev[n][j][1].record(stream)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
-        times = [0.0] * len(launches)
-        for _ in range(reps):
-            for j, L in enumerate(launches):
-                ev[j][0].record(stream)
-                fn(L)
-                ev[j][1].record(stream)
-            torch.cuda.synchronize()
+        if rep == 0:
+            continue
+        for n in names:
             for j in range(len(launches)):
-                times[j] += ev[j][0].elapsed_time(ev[j][1]) / reps
+                times[n][j] += ev[n][j][0].elapsed_time(ev[n][j][1]) / reps
+    out = {}
+    for name in names:
         flops = KERNEL_UNITS[name] * sum(L[4] for L in launches) / len(launches)
-        avg_ms = sum(times) / len(launches)
+        avg_ms = sum(times[name]) / len(launches)
         out[name] = {"avg_launch_ms": round(avg_ms, 4), "launches": len(launches),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 5),
                      "achieved_tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2),
                      "frac": round(flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "total_ms_per_pass": round(sum(times), 4)}
+                     "total_ms_per_pass": round(sum(times[name]), 4)}
     return out
 
 
 # The files the chunk kernels' code and parameter block come from: the stored counter readings
 # describe these kernels and stay valid while these files do.
-CHUNK_KERNEL_SOURCES = ("kern_bwd.hip", "kern_common.h", "kern_fwd.hip", "ra_internal.h")
+CHUNK_KERNEL_SOURCES = ("kern_bwd.hip", "kern_common.h", "kern_fwd.hip", "ra_internal.h", "ra_host.cpp",
+                        "ra_plan.cpp")
 
 
 def source_hash():
@@ -217,10 +231,12 @@ def stored_traffic(wl_name, kernel):
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
-def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes):
+def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes, stage_bytes):
     """Turns two rocprofv3 --pmc runs of `--kernels-only` (FETCH_SIZE, then WRITE_SIZE; KiB per
-    dispatch) into bytes per launch, scaled by what the counters read for the calibration copy
-    (the layout kernel gathering one K tensor: calib_bytes read and calib_bytes written)."""
+    dispatch) into bytes per launch, scaled by what the counters read for a calibration copy:
+    the layout kernel gathering one K tensor (calib_bytes read and written).  The staging copy
+    (copy2d_kernel, stage_bytes read and written per dispatch, a different kernel and size)
+    gives a second, independent factor; the record keeps both."""
     import csv
     import glob
     import re
@@ -231,7 +247,7 @@ def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] != counter:
                     continue
-                m = re.search(r"(chunk_\w+|layout_kernel)", r["Kernel_Name"])
+                m = re.search(r"(chunk_\w+|layout_kernel|copy2d_kernel)", r["Kernel_Name"])
                 if not m:
                     continue
                 a = acc.setdefault(m.group(1), {})
@@ -246,6 +262,11 @@ def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes):
                            "fetch_scale": fs, "write_scale": ws},
            "kernels": {k: {"fetch_bytes_per_launch": fetch[k] * fs, "write_bytes_per_launch": write[k] * ws}
                        for k in fetch if k.startswith("chunk_") and k in write}}
+    if "copy2d_kernel" in fetch and "copy2d_kernel" in write:
+        rec["check"] = {"kernel": "copy2d_kernel", "bytes_each_way": stage_bytes,
+                        "fetch_read": fetch["copy2d_kernel"], "write_read": write["copy2d_kernel"],
+                        "fetch_scale": stage_bytes / fetch["copy2d_kernel"],
+                        "write_scale": stage_bytes / write["copy2d_kernel"]}
     with open(traffic_path(wl_name), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -258,6 +279,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' rank views")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--same-stream", action="store_true", help="stage K/V on the compute stream")
     ap.add_argument("--window", type=int, default=0, help="sliding window (0 = plain causal)")
@@ -274,7 +296,8 @@ def main():
         wl = WORKLOADS[args.workload]
         esize = 2 if wl.dtype == "bf16" else 4
         traffic_summary(wl.name, args.traffic_summary[0], args.traffic_summary[1],
-                        wl.batch * wl.heads_kv * wl.seq_len * wl.head_dim * esize)
+                        wl.batch * wl.heads_kv * wl.seq_len * wl.head_dim * esize,
+                        wl.batch * wl.heads_kv * (wl.seq_len // wl.cp) * wl.head_dim * esize)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs a single rank view at a time on one "
@@ -286,107 +309,130 @@ def main():
     from context_blockwise_causal_amd import api
     from context_blockwise_causal_amd.inputs import draw
     from context_blockwise_causal_amd.workloads import WORKLOADS
-    from tests.gpu_util import to_dev
 
-    wl = WORKLOADS[args.workload]
-    prob = api.Problem(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.cp,
-                       wl.layout, wl.dtype, 0.0, args.window, args.attn_chunk)
-    t = draw(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.dtype, wl.seed,
-             with_grad=True)
     ctx = api.Context(0)
-    dev = {n: to_dev(t.store[n], wl.dtype) for n in ("q", "k", "v", "do")}
     compute = torch.cuda.current_stream()
-    staging = compute if args.same_stream else torch.cuda.Stream()
+    draws = {}
 
-    # buffers allocated once, outside the timed region
-    k_ring = torch.empty_like(dev["k"])
-    v_ring = torch.empty_like(dev["v"])
-    bufs = {}
-    for r in wl.ranks:
-        q_sl = torch.empty((wl.batch, wl.heads_q, prob.chunk, wl.head_dim), dtype=prob.torch_dtype,
-                           device="cuda")
-        bufs[r] = dict(q=q_sl, do=torch.empty_like(q_sl), o=torch.empty_like(q_sl),
-                       lse=torch.empty(q_sl.shape[:3], dtype=torch.float32, device="cuda"),
-                       dq=torch.empty_like(q_sl), dk=torch.empty_like(k_ring), dv=torch.empty_like(v_ring))
-    ws_fwd = api.workspace(prob, 0)
-    ws_bwd = api.workspace(prob, 1) if wl.backward else None
+    def drawn(wl):
+        key = (wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.dtype, wl.seed)
+        if key not in draws:
+            draws.clear()
+            draws[key] = draw(*key, with_grad=True)
+        return draws[key]
 
-    def fwd(r):
-        b = bufs[r]
-        api.ra_rank_view_fwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], ws_fwd,
-                             compute, staging)
-
-    def bwd(r):
-        b = bufs[r]
-        api.ra_rank_view_bwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], b["do"],
-                             b["dq"], b["dk"], b["dv"], ws_bwd, compute, staging)
-
-    def step():
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["k"], k_ring)
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["v"], v_ring)
-        for r in wl.ranks:
-            api.ra_layout_gather(ctx, prob, r, 1, dev["q"], bufs[r]["q"])
-            if wl.backward:
-                api.ra_layout_gather(ctx, prob, r, 1, dev["do"], bufs[r]["do"])
-            fwd(r)
-            if wl.backward:
-                bwd(r)
-
-    def timed(fn, reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record(compute)
-        for _ in range(reps):
+    def timed_each(fn, reps, warm=1):
+        """Median and all durations (ms) of `reps` calls of fn, each bracketed by events on the
+        compute stream."""
+        for _ in range(warm):
             fn()
-        ev[1].record(compute)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / reps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(compute)
+            fn()
+            b.record(compute)
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in ev]
+        return statistics.median(ts), ts
+
+    def workload(name, window=0, attn_chunk=0):
+        """Device buffers and the step functions of one workload (allocated outside timing)."""
+        wl = WORKLOADS[name]
+        prob = api.Problem(wl.batch, wl.seq_len, wl.heads_q, wl.heads_kv, wl.head_dim, wl.cp,
+                           wl.layout, wl.dtype, 0.0, window, attn_chunk)
+        t = drawn(wl)
+        dev = {n: api.to_device(t.store[n], wl.dtype) for n in ("q", "k", "v", "do")}
+        staging = compute if args.same_stream else torch.cuda.Stream()
+        k_ring = torch.empty_like(dev["k"])
+        v_ring = torch.empty_like(dev["v"])
+        bufs = {}
+        for r in wl.ranks:
+            q_sl = torch.empty((wl.batch, wl.heads_q, prob.chunk, wl.head_dim), dtype=prob.torch_dtype,
+                               device="cuda")
+            bufs[r] = dict(q=q_sl, do=torch.empty_like(q_sl), o=torch.empty_like(q_sl),
+                           lse=torch.empty(q_sl.shape[:3], dtype=torch.float32, device="cuda"),
+                           dq=torch.empty_like(q_sl), dk=torch.empty_like(k_ring), dv=torch.empty_like(v_ring))
+        ws_fwd = api.workspace(prob, 0)
+        ws_bwd = api.workspace(prob, 1) if wl.backward else None
+
+        def fwd(r):
+            b = bufs[r]
+            api.ra_rank_view_fwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], ws_fwd,
+                                 compute, staging)
+
+        def bwd(r):
+            b = bufs[r]
+            api.ra_rank_view_bwd(ctx, prob, r, b["q"], k_ring, v_ring, b["o"], b["lse"], b["do"],
+                                 b["dq"], b["dk"], b["dv"], ws_bwd, compute, staging)
+
+        def gathers():
+            api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["k"], k_ring)
+            api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["v"], v_ring)
+            for r in wl.ranks:
+                api.ra_layout_gather(ctx, prob, r, 1, dev["q"], bufs[r]["q"])
+                if wl.backward:
+                    api.ra_layout_gather(ctx, prob, r, 1, dev["do"], bufs[r]["do"])
+
+        def step():
+            gathers()
+            for r in wl.ranks:
+                fwd(r)
+                if wl.backward:
+                    bwd(r)
+
+        fwd_flops = sum(sum(counted_flops(api, prob, r)) for r in wl.ranks)
+        return dict(wl=wl, prob=prob, t=t, dev=dev, k_ring=k_ring, v_ring=v_ring, bufs=bufs, fwd=fwd,
+                    bwd=bwd, step=step, gathers=gathers, fwd_flops=fwd_flops)
+
+    def rates(W, steps, warmup):
+        """Step (fwd+bwd over every rank view) and per-pass medians, counted TFLOP/s."""
+        wl = W["wl"]
+        ff = W["fwd_flops"]
+        total = ff * (3.5 if wl.backward else 1.0)
+        for _ in range(warmup):
+            W["step"]()
+        step_ms, step_all = timed_each(W["step"], steps, warm=0)
+        fwd_ms, _ = timed_each(lambda: [W["fwd"](r) for r in wl.ranks], max(3, steps))
+        out = {"ms_per_step": step_ms, "step_ms_all": [round(x, 4) for x in step_all],
+               "tflops": total / (step_ms * 1e-3) / 1e12, "counted_tflop_per_step": total / 1e12,
+               "fwd_ms": fwd_ms, "fwd_tflops": ff / (fwd_ms * 1e-3) / 1e12}
+        if wl.backward:
+            bwd_ms, _ = timed_each(lambda: [W["bwd"](r) for r in wl.ranks], max(3, steps))
+            out["bwd_ms"] = bwd_ms
+            out["bwd_tflops"] = 2.5 * ff / (bwd_ms * 1e-3) / 1e12
+        return out
+
+    def frac(x):
+        return round(x / PEAK_BF16_TFLOPS, 4)
+
+    W = workload(args.workload, args.window, args.attn_chunk)
+    wl, prob, bufs = W["wl"], W["prob"], W["bufs"]
 
     if args.kernels_only:
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["k"], k_ring)
-        api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["v"], v_ring)
+        W["gathers"]()
         for r in wl.ranks:
-            api.ra_layout_gather(ctx, prob, r, 1, dev["q"], bufs[r]["q"])
-            api.ra_layout_gather(ctx, prob, r, 1, dev["do"], bufs[r]["do"])
-            fwd(r)
-        launches = chunk_launches(api, prob, wl, k_ring, v_ring)
-        rates = kernel_rates(api, ctx, prob, wl, bufs, launches, compute, wl.backward, reps=1)
+            W["fwd"](r)
+        launches = chunk_launches(api, prob, wl, W["k_ring"], W["v_ring"])
+        kr = kernel_rates(api, ctx, prob, wl, bufs, launches, compute, wl.backward, reps=1)
+        # the calibration copies of the traffic record: the layout gather of K and one staging copy
+        api.ra_layout_gather(ctx, prob, 0, wl.cp, W["dev"]["k"], W["k_ring"])
+        api.ra_stage_kv(ctx, prob, 0, W["k_ring"], W["v_ring"])
         torch.cuda.synchronize()
-        print(json.dumps({"kernels_only": wl.name, "kernels": rates}), flush=True)
+        print(json.dumps({"kernels_only": wl.name, "kernels": kr}), flush=True)
         ctx.close()
         return
 
-    fwd_flops = {r: sum(counted_flops(api, prob, r)) for r in wl.ranks}
-    total_fwd = sum(fwd_flops.values())
-    total = total_fwd * (3.5 if wl.backward else 1.0)
+    # ---- the headline: whole steps of the workload, median step time
+    R = rates(W, args.steps, args.warmup)
+    value = R["tflops"]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    step_ms = timed(step, args.steps)
-
-    # per-pass rates, timed separately (same launches as inside the step)
-    fwd_ms = timed(lambda: [fwd(r) for r in wl.ranks], max(2, args.steps))
-    bwd_ms = timed(lambda: [bwd(r) for r in wl.ranks], max(2, args.steps)) if wl.backward else None
-
-    # all-gather mode with split-KV: the same forward rank views, chunks computed concurrently
-    # into partials and merged on a second stream
-    ws_split = api.workspace(prob, 2)
-    merge_stream = torch.cuda.Stream()
-
-    def fwd_split(r):
-        b = bufs[r]
-        api.rank_view_fwd_split(ctx, prob, r, b["q"], k_ring, v_ring, ws=ws_split, compute=compute,
-                                merge=merge_stream, out=(b["o"], b["lse"]))
-    fwd_split_ms = timed(lambda: [fwd_split(r) for r in wl.ranks], max(2, args.steps))
-    del ws_split
-
-    # each chunk kernel on its own: replay the workload's chunk launches with events on the
-    # launch stream; the dominant kernel (most time per pass) gives the roofline entry.
-    launches = chunk_launches(api, prob, wl, k_ring, v_ring)
-    rates = kernel_rates(api, ctx, prob, wl, bufs, launches, compute, wl.backward)
-    dom = max(rates, key=lambda k: rates[k]["total_ms_per_pass"])
-    d = rates[dom]
+    # ---- each chunk kernel on its own (event-timed replays of the workload's launches)
+    launches = chunk_launches(api, prob, wl, W["k_ring"], W["v_ring"])
+    kr = kernel_rates(api, ctx, prob, wl, bufs, launches, compute, wl.backward)
+    del launches
+    dom = max(kr, key=lambda k: kr[k]["total_ms_per_pass"])
+    d = kr[dom]
     traffic = stored_traffic(wl.name, dom)
     roof = {"kernel": dom, "bound": "mfma", "achieved": d["achieved_tflops"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": d["frac"],
@@ -395,31 +441,67 @@ def main():
             "algorithmic_tflop_per_launch": d["algorithmic_tflop_per_launch"],
             "launches": d["launches"]}
 
-    # HBM-bound helpers: the layout gather of K (read + write) and one merge over the Q slice
+    # ---- split-KV all-gather forward (the chunks computed concurrently into partials)
+    ws_split = api.workspace(prob, 2)
+    merge_stream = torch.cuda.Stream()
+
+    def fwd_split():
+        for r in wl.ranks:
+            b = bufs[r]
+            api.rank_view_fwd_split(ctx, prob, r, b["q"], W["k_ring"], W["v_ring"], ws=ws_split,
+                                    compute=compute, merge=merge_stream, out=(b["o"], b["lse"]))
+    split_ms, _ = timed_each(fwd_split, 3)
+    del ws_split
+
+    # ---- HBM-bound steps, cold (after writing a 2 GiB buffer, more than the 256 MB MALL and the
+    # L2s hold) and warm (back to back)
     esize = 2 if wl.dtype == "bf16" else 4
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+
+    def cold_warm(fn, nbytes, reps=5):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            flush.fill_(1)
+            a.record(compute)
+            fn()
+            b.record(compute)
+        torch.cuda.synchronize()
+        cold = statistics.median(a.elapsed_time(b) for a, b in ev)
+        warm, _ = timed_each(fn, reps)
+        return {"bytes": nbytes, "cold_ms": round(cold, 4), "cold_gbs": round(nbytes / (cold * 1e-3) / 1e9, 1),
+                "warm_ms": round(warm, 4), "warm_gbs": round(nbytes / (warm * 1e-3) / 1e9, 1)}
+
+    hbm = {"peak_gbs": PEAK_HBM_GBS}
     kbytes = 2 * wl.batch * wl.heads_kv * wl.seq_len * wl.head_dim * esize
-    gather_ms = timed(lambda: api.ra_layout_gather(ctx, prob, 0, wl.cp, dev["k"], k_ring), 5)
-    rows = prob.chunk
-    U, m, l = api.new_state(prob, rows)
+    hbm["layout_gather_k"] = cold_warm(lambda: api.ra_layout_gather(ctx, prob, 0, wl.cp, W["dev"]["k"], W["k_ring"]),
+                                       kbytes)
+    stage_dst = torch.empty((2, wl.batch, wl.heads_kv, prob.chunk, wl.head_dim), dtype=prob.torch_dtype,
+                            device="cuda")
+    sbytes = 2 * stage_dst.numel() * esize
+    hbm["staging_copy"] = cold_warm(lambda: api.ra_stage_kv(ctx, prob, 1 % wl.cp, W["k_ring"], W["v_ring"], stage_dst),
+                                    sbytes)
+    del stage_dst
+    U, m, l = api.new_state(prob, prob.chunk)
     api.ra_state_init(ctx, prob, U, m, l)
     o_part = torch.zeros_like(U)
     lse_part = torch.zeros_like(m)
-    merge_ms = timed(lambda: api.ra_lse_merge(ctx, prob, o_part, lse_part, U, m, l), 5)
-    merge_bytes = wl.batch * wl.heads_q * rows * (12 * wl.head_dim + 20)
+    hbm["lse_merge"] = cold_warm(lambda: api.ra_lse_merge(ctx, prob, o_part, lse_part, U, m, l),
+                                 wl.batch * wl.heads_q * prob.chunk * (12 * wl.head_dim + 20))
+    del U, m, l, o_part, lse_part
     # Ulysses re-shard at the Qwen3-shaped share's source: 32 query heads over an all-to-all of
     # 8, full sequence 65536 (the receive buffer of one rank unpacked to its 4-head shard)
     uprob = api.Problem(1, 65536, 32, 8, 128, 8, "contiguous", "bf16")
     ushape = api.reshard_shapes(uprob, 1, 32)
     usrc = torch.zeros(ushape[0], dtype=torch.bfloat16, device="cuda")
     udst = torch.empty(ushape[1], dtype=torch.bfloat16, device="cuda")
-    reshard_ms = timed(lambda: api.ra_ulysses_reshard(ctx, uprob, 1, 32, usrc, udst), 5)
-    reshard_bytes = 2 * usrc.numel() * 2
-    del usrc, udst
+    hbm["ulysses_reshard"] = cold_warm(lambda: api.ra_ulysses_reshard(ctx, uprob, 1, 32, usrc, udst),
+                                       2 * usrc.numel() * 2)
+    hbm["ulysses_reshard"]["shape"] = "head unpack, (8, 1, 4, 8192, 128) bf16 -> (1, 4, 65536, 128)"
+    del usrc, udst, flush
 
-    value = total / (step_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(R["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic: seeded N(0,1) Q/K/V/dO, bf16 round-to-nearest-even; model shapes only",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
@@ -427,35 +509,45 @@ def main():
                    "cp": wl.cp, "layout": wl.layout, "ranks": list(wl.ranks),
                    "passes": "fwd+bwd" if wl.backward else "fwd",
                    "window": args.window, "attn_chunk": args.attn_chunk},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd_tflops": round(total_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-        "fwd_frac_of_peak": round(total_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "counted_tflop_per_step": round(total / 1e12, 4),
+        "timing": "median over the timed steps of HIP events on the compute stream",
+        "step_ms_all": R["step_ms_all"],
+        "frac_of_peak": frac(value),
+        "fwd_tflops": round(R["fwd_tflops"], 2), "fwd_frac_of_peak": frac(R["fwd_tflops"]),
+        "counted_tflop_per_step": round(R["counted_tflop_per_step"], 4),
     }
-    out["split_kv_fwd"] = {"ms": round(fwd_split_ms, 4),
-                           "tflops": round(total_fwd / (fwd_split_ms * 1e-3) / 1e12, 2),
-                           "ring_fwd_ms": round(fwd_ms, 4)}
     if wl.backward:
-        bt = total_fwd * 2.5 / (bwd_ms * 1e-3) / 1e12
-        out["bwd_tflops"] = round(bt, 2)
-        out["bwd_frac_of_peak"] = round(bt / PEAK_BF16_TFLOPS, 4)
+        out["bwd_tflops"] = round(R["bwd_tflops"], 2)
+        out["bwd_frac_of_peak"] = frac(R["bwd_tflops"])
+    out["split_kv_fwd"] = {"ms": round(split_ms, 4), "tflops": round(W["fwd_flops"] / (split_ms * 1e-3) / 1e12, 2),
+                           "ring_fwd_ms": round(R["fwd_ms"], 4)}
     out["roofline"] = roof
-    out["kernels"] = rates
-    out["hbm_kernels"] = {
-        "layout_gather": {"gbs": round(kbytes / (gather_ms * 1e-3) / 1e9, 1), "bytes": kbytes,
-                          "ms": round(gather_ms, 4)},
-        "lse_merge": {"gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1), "bytes": merge_bytes,
-                      "ms": round(merge_ms, 4)},
-        "ulysses_reshard": {"gbs": round(reshard_bytes / (reshard_ms * 1e-3) / 1e9, 1), "bytes": reshard_bytes,
-                            "ms": round(reshard_ms, 4),
-                            "shape": "head unpack, (8, 1, 4, 8192, 128) bf16 -> (1, 4, 65536, 128)"},
-        "peak_gbs": PEAK_HBM_GBS}
-    if "chunk_fwd_bf16_kernel" in rates:
-        fwd_chunk_ms = rates["chunk_fwd_bf16_kernel"]["total_ms_per_pass"]
-        out["staging_overlap"] = {"rank_views_fwd_ms": round(fwd_ms, 4), "chunk_kernels_fwd_ms": fwd_chunk_ms,
-                                  "ratio": round(fwd_chunk_ms / fwd_ms, 4)}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, t, args.cpu_seconds)
+    out["kernels"] = kr
+    out["hbm_kernels"] = hbm
+    if "chunk_fwd_bf16_kernel" in kr:
+        fk = kr["chunk_fwd_bf16_kernel"]["total_ms_per_pass"]
+        out["staging_overlap"] = {"rank_views_fwd_ms": round(R["fwd_ms"], 4), "chunk_kernels_fwd_ms": fk,
+                                  "ratio": round(fk / R["fwd_ms"], 4)}
+    if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
+        out["cpu_baseline"] = cpu_baseline(wl, W["t"], args.cpu_seconds)
+    del W, bufs, R
+    torch.cuda.empty_cache()
+
+    # ---- the other long-sequence workloads, rank views only
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+        other = {}
+        for name in EXTRA_WORKLOADS:
+            W2 = workload(name)
+            R2 = rates(W2, 3, 1)
+            o = {"ms_per_step": round(R2["ms_per_step"], 4), "tflops": round(R2["tflops"], 2),
+                 "frac_of_peak": frac(R2["tflops"]), "fwd_tflops": round(R2["fwd_tflops"], 2),
+                 "fwd_frac_of_peak": frac(R2["fwd_tflops"])}
+            if "bwd_tflops" in R2:
+                o["bwd_tflops"] = round(R2["bwd_tflops"], 2)
+                o["bwd_frac_of_peak"] = frac(R2["bwd_tflops"])
+            other[name] = o
+            del W2
+            torch.cuda.empty_cache()
+        out["other_workloads"] = other
     ctx.close()
     print(json.dumps(out), flush=True)
 

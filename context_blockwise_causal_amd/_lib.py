@@ -61,6 +61,7 @@ SIGNATURES = {
     "ra_layout_gather": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
     "ra_layout_scatter": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
     "ra_ulysses_reshard": [_P, _PROB, _I32, _I64, _P, _P, _P],
+    "ra_stage_kv": [_P, _PROB, _I32, _P, _P, _P, _P],
     "ra_state_init": [_P, _PROB, _I64, _FP, _FP, _FP, _P],
     "ra_chunk_fwd": [_P, _PROB, _P, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP, _FP, _P],
     "ra_lse_merge": [_P, _PROB, _I64, _FP, _FP, _FP, _FP, _FP, _P],
@@ -68,6 +69,9 @@ SIGNATURES = {
     "ra_bwd_preprocess": [_P, _PROB, _I64, _P, _P, _FP, _P],
     "ra_chunk_bwd": [_P, _PROB, _P, _P, _FP, _FP, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP,
                      _FP, _P],
+    "ra_chunk_bwd_ds_size": [_PROB, _I64, _I64, _PAIRS, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "ra_chunk_bwd_ds": [_P, _PROB, _P, _P, _FP, _FP, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP,
+                        _FP, _P, ctypes.c_size_t, _P],
     "ra_cast_from_f32": [_P, _PROB, _I64, _FP, _P, _P],
     "ra_rank_view_fwd": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],
     "ra_rank_view_fwd_split": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],

@@ -45,6 +45,16 @@ class Problem:
                          self.cp, self.layout, self.dtype, self.scale, self.window, self.attn_chunk)
 
 
+def to_device(store_array, dtype: str, device="cuda"):
+    """A store-form numpy array (float32, or uint16 bf16 bit patterns as drawn by ``inputs``) as
+    a device tensor of the problem dtype, bits unchanged."""
+    import numpy as np
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(store_array).view(np.int16))
+        return t.to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(store_array, dtype=np.float32)).to(device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -171,6 +181,23 @@ def ra_ulysses_reshard(ctx, prob: Problem, step: int, heads: int, src, dst=None,
     return dst
 
 
+def ra_stage_kv(ctx, prob: Problem, owner: int, k_ring, v_ring, dst=None, stream=None):
+    """Owner's K and V chunk out of the ring tensors into `dst` (K then V): a uint8-viewable
+    device tensor of 2 * batch * heads_kv * chunk * head_dim elements of the problem dtype
+    (allocated here when None, shaped (2, batch, heads_kv, chunk, head_dim))."""
+    kshp = (prob.batch, prob.heads_kv, prob.seq_len, prob.head_dim)
+    _need(k_ring, kshp, prob.torch_dtype, "k_ring")
+    _need(v_ring, kshp, prob.torch_dtype, "v_ring")
+    shp = (2, prob.batch, prob.heads_kv, prob.chunk, prob.head_dim)
+    if dst is None:
+        dst = torch.empty(shp, dtype=prob.torch_dtype, device=k_ring.device)
+    _need(dst, shp, prob.torch_dtype, "dst")
+    p = prob.c()
+    L.call("ra_stage_kv", ctx.handle, ctypes.byref(p), owner, _ptr(k_ring), _ptr(v_ring), _ptr(dst),
+           _stream(stream))
+    return dst
+
+
 def new_state(prob: Problem, rows: int, device="cuda"):
     U = torch.empty((prob.batch, prob.heads_q, rows, prob.head_dim), dtype=torch.float32, device=device)
     m = torch.empty((prob.batch, prob.heads_q, rows), dtype=torch.float32, device=device)
@@ -268,6 +295,48 @@ def ra_chunk_bwd(ctx, prob: Problem, q, dO, lse, delta, k, v, pairs, dq_acc, dk_
     L.call("ra_chunk_bwd", ctx.handle, ctypes.byref(p), _ptr(q), _ptr(dO), _ptr(lse), _ptr(delta),
            q_rows, _ptr(k), _ptr(v), kv_rows, arr, len(pairs), _ptr(dq_acc), _ptr(dk_acc),
            _ptr(dv_acc), _stream(stream))
+
+
+def ra_chunk_bwd_ds_size(prob: Problem, q_rows: int, kv_rows: int, pairs) -> int:
+    """Scratch bytes of ra_chunk_bwd_ds for this pair list (0 for fp32 problems)."""
+    p = prob.c()
+    arr = L.pairs_array(pairs)
+    n = ctypes.c_size_t()
+    L.call("ra_chunk_bwd_ds_size", ctypes.byref(p), q_rows, kv_rows, arr, len(pairs), ctypes.byref(n))
+    return n.value
+
+
+def ra_chunk_bwd_ds(ctx, prob: Problem, q, dO, lse, delta, k, v, pairs, dq_acc, dk_acc, dv_acc,
+                    scratch=None, stream=None):
+    """Chunk backward with stored dS: dK/dV kernel (which stores dS) then dQ = dS K.  dq_acc =
+    None runs the first kernel only, dk_acc = dv_acc = None the second only (reading the scratch
+    of an earlier first-phase call).  `scratch` is a uint8 device tensor of at least
+    ra_chunk_bwd_ds_size bytes (allocated here when None)."""
+    q_rows = q.shape[2]
+    kv_rows = k.shape[2]
+    qs = (prob.batch, prob.heads_q, q_rows)
+    ks = (prob.batch, prob.heads_kv, kv_rows, prob.head_dim)
+    _need(q, qs + (prob.head_dim,), prob.torch_dtype, "q")
+    _need(dO, qs + (prob.head_dim,), prob.torch_dtype, "dO")
+    _need(lse, qs, torch.float32, "lse")
+    _need(delta, qs, torch.float32, "delta")
+    _need(k, ks, prob.torch_dtype, "k")
+    _need(v, ks, prob.torch_dtype, "v")
+    if dq_acc is not None:
+        _need(dq_acc, qs + (prob.head_dim,), torch.float32, "dq_acc")
+    if dk_acc is not None:
+        _need(dk_acc, ks, torch.float32, "dk_acc")
+    if dv_acc is not None:
+        _need(dv_acc, ks, torch.float32, "dv_acc")
+    if scratch is None:
+        nbytes = ra_chunk_bwd_ds_size(prob, q_rows, kv_rows, pairs)
+        scratch = torch.empty(max(16, nbytes), dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    arr = L.pairs_array(pairs)
+    L.call("ra_chunk_bwd_ds", ctx.handle, ctypes.byref(p), _ptr(q), _ptr(dO), _ptr(lse), _ptr(delta),
+           q_rows, _ptr(k), _ptr(v), kv_rows, arr, len(pairs), _ptr(dq_acc), _ptr(dk_acc),
+           _ptr(dv_acc), _ptr(scratch), scratch.numel(), _stream(stream))
+    return scratch
 
 
 def ra_cast_from_f32(ctx, prob: Problem, src, dst=None, stream=None):

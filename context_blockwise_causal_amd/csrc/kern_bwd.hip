@@ -36,6 +36,15 @@ constexpr int kNT = 256;
 
 constexpr int kKvBN = 128;  // keys per workgroup
 constexpr int kKvBQ = 32;   // query rows per step
+constexpr int kDsStage = kKvBQ * kKvBN;  // elements of one staged dS block (32 queries x 128 keys)
+
+// Staged dS block: row q (query of the step) holds the 128 keys of the workgroup in 16-byte
+// chunks; chunk c of row q sits at chunk position c ^ (4 ((q >> 3) & 1)), which keeps the 2-byte
+// writes of a step (one row per lane half, rows 8 apart) and the 16-byte row reads of the
+// store on distinct banks.
+__device__ __forceinline__ int stage_off(int q, int key) {
+  return q * kKvBN + ((((key >> 3) ^ (((q >> 3) & 1) << 2))) << 3) + (key & 7);
+}
 
 template <int D>
 struct KvCfg {
@@ -90,9 +99,14 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   // __restrict__ parameter, which lets the compiler prove that those loads do not alias its reads
   // (so it does not wait for them before the step's LDS reads).  One array, not several: with
   // several LDS variables the compiler's LDS lowering replaces the pointer-based alias scopes.
-  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT];
+  // Two more blocks of 32 queries x 128 keys stage the workgroup's scale * dS for the dQ pass:
+  // each step's wavefronts write their 32 x 32 blocks there, and the next step stores the whole
+  // block query-major (256 contiguous bytes per query row), which takes a quarter of the cache
+  // lines per store instruction that per-lane key rows would.
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT + 2 * kDsStage];
   u16* const vt = lds;
   u16* const qdbuf = lds + kKvBN * D;
+  u16* const stage = qdbuf + 4 * C::QT;
 
   const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -150,13 +164,34 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
     const float* lsep = p.lse + qhead + pr.q_row0;
     const float* dltp = p.delta + qhead + pr.q_row0;
-
+    // Stored scale * dS (bf16, query-major: q_len rows of ds_ld keys) of this (batch, query head)
+    // and pair, at this workgroup's first key.
+    u16* const dsp = p.ds ? reinterpret_cast<u16*>(p.ds) + pr.ds_off +
+                                ((int64_t)tr.b * p.Hq + tr.hq) * pr.q_len * pr.ds_ld + kloc0
+                          : nullptr;
     // One query step on (Qs, dOs, ex); the next step's rows go into (nQ, ndO, nex).
     // (la, ld): raw lse / delta of this step's rows, loaded one step ahead.
     float la, ld;
+    // Stores the dS block staged by the step at query qb: thread t moves 16-byte chunks t and
+    // t + 256 (row = chunk / 16, 16 chunks per row), rows past the pair skipped.  Waves that were
+    // inactive in that step left stale values in their keys' columns; those (query, key) entries
+    // are excluded by the mask, and the dQ pass masks them out again.
+    auto flush_ds = [&](const u16* __restrict__ blk, int64_t qb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int idx = tid + 256 * h, row = idx >> 4, ch = idx & 15;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(blk + row * kKvBN + ((ch ^ (((row >> 3) & 1) << 2)) << 3));
+        if (qb + row < pr.q_len)
+          __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(dsp + (qb + row) * pr.ds_ld + ch * 8));
+      }
+    };
     auto step = [&](const u16* __restrict__ Vs, const u16* __restrict__ Qs, const u16* __restrict__ dOs,
-                    u16* __restrict__ nQ, u16* __restrict__ ndO, int it) {
+                    u16* __restrict__ nQ, u16* __restrict__ ndO, u16* __restrict__ sw,
+                    const u16* __restrict__ sr, int it) {
       const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
+      // the previous step's dS block goes out before this step's loads, so that the loads' wait at
+      // the end of the step finds the stores long done
+      if (dsp && it > 0) flush_ds(sr, qbase - kKvBQ);
       // this lane's broadcast values: lse in base 2 (+inf past the pair, so that P vanishes) and
       // delta (0 past the pair)
       const bool rv = qbase + perm_reg_row(lane & 15, hh) < pr.q_len;
@@ -221,6 +256,18 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
             dv_acc[db] = mfma32(tr_operand(dOs, ta, D, c, db), pb[c], dv_acc[db]);
             dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
+        // scale * dS (bf16, exactly the operand of dK) into the staged block for the dQ pass:
+        // register 8c + e of this lane is query 16 c + 8 hh + e of the step, at its key's column
+        // (extracted through 32-bit words)
+        if (dsp) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 wv = __builtin_bit_cast(u32x4, dsb[c]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              sw[stage_off(16 * c + 8 * hh + e, kl)] = (u16)(wv[e >> 1] >> (16 * (e & 1)));
+          }
+        }
       }
       wait_vmem();
       __syncthreads();
@@ -234,8 +281,11 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     for (int it = 0; it < niter; ++it) {
       u16* cur = qdbuf + (it & 1) * 2 * C::QT;
       u16* nxt = qdbuf + ((it + 1) & 1) * 2 * C::QT;
-      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, it);
+      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, stage + (it & 1) * kDsStage,
+           stage + ((it + 1) & 1) * kDsStage, it);
     }
+    // the last step's block (its writes are complete: the step ended with a barrier)
+    if (dsp) flush_ds(stage + ((niter - 1) & 1) * kDsStage, q_begin + (int64_t)(niter - 1) * kKvBQ);
   }
 
   // The query heads of one key/value head add into the same dK/dV rows, so the sums go out as
@@ -446,6 +496,171 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
   }
 }
 
+// ======================================================================= dQ from stored dS
+//
+// The dK/dV kernel writes scale * dS (bf16, the operand it feeds to dK) query-major, one row of
+// keys per query.  dQ is then the plain contraction dQ += (scale dS) K: one workgroup = 4
+// wavefronts = 128 query rows of one (batch, head), a lane one query; per tile of 64 keys the K
+// tile and the workgroup's 128 x 64 block of dS are staged in LDS (direct loads, one tile ahead)
+// and dQ^T += K^T dS^T, K^T read transposed and dS^T as row reads (a lane's query row holds its
+// keys contiguously).  The kernel is bound by reading dS from HBM (two bytes per (query, key) pair
+// against 2 D FLOPs).
+//
+// Entries of dS that no query of a pair sees may never have been written, or hold stale values
+// (the dK/dV kernel skips query steps that lie wholly before its keys or past their window, and
+// wavefronts whose keys a step does not reach leave their columns of the staged block as they
+// were), so tiles that straddle a mask bound zero the excluded entries of the operand before the
+// MFMA; interior tiles are fully visible and were written.
+
+constexpr int kDsBM = 128;  // query rows per workgroup (= columns of a stored dS^T row block)
+constexpr int kDsBN = 64;   // keys per tile
+
+template <int D>
+__global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p) {
+  constexpr int DB = D / 32;
+  constexpr int KT = kDsBN * D;       // elements of one K tile
+  constexpr int ST = kDsBM * kDsBN;   // elements of one dS tile (128 queries x 64 keys)
+  // two buffers of (K tile, dS^T tile), read and filled through __restrict__ pointers
+  __shared__ __attribute__((aligned(16))) u16 buf[2 * (KT + ST)];
+
+  const TileRef tr = map_tile(p, kDsBM);
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int qi = 32 * w + lq;
+  const bool qvalid = qi < tr.nrows;
+  const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
+  const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
+  const int64_t head = (int64_t)tr.b * p.Hq + tr.hq;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+  const TrAddr kt = make_tr_addr(lane, D);          // K^T out of the [key][d] tile
+  const RowAddr sa = make_row_addr(qi, hh, kDsBN);  // this lane's query row of the dS tile
+  const u16* Kg = reinterpret_cast<const u16*>(p.k);
+  const KRange& R = p.ranges[tr.range];
+  for (int pi = 0; pi < R.npairs; ++pi) {
+    const KPair pr = p.pairs[R.pair[pi]];
+    const bool diag = pr.mask == RA_MASK_DIAG;
+    const int64_t qloc0 = tr.row0 - pr.q_row0;
+    const int64_t iq = qloc0 + qi;
+    int64_t key_end = pr.kv_len;
+    if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
+    const int nkt = (int)((key_end + kDsBN - 1) / kDsBN);
+    const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
+    // this workgroup's 128 query rows of the pair's dS block (rows of ds_ld keys)
+    const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + (head * pr.q_len + qloc0) * pr.ds_ld;
+    const int64_t q_left = pr.q_len - qloc0;  // valid query rows of the tile
+    const int64_t wq_first = qloc0 + 32 * w;
+    const bool wave_has_rows = 32 * w < tr.nrows;
+    const bool has_lo = p.window > 0 || p.attn_chunk > 0;
+    int64_t lo = 0, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
+    if (has_lo) {
+      lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo = lowest_key(pr.q_pos0 + wq_first, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 31, p.window, p.attn_chunk) - pr.kv_pos0;
+      const int64_t tile_lo = lowest_key(pr.q_pos0 + qloc0, p.window, p.attn_chunk) - pr.kv_pos0;
+      kt0 = tile_lo > 0 ? tile_lo / kDsBN : 0;
+    }
+
+    auto step = [&](const u16* __restrict__ kb, const u16* __restrict__ sb, u16* __restrict__ nk,
+                    u16* __restrict__ ns, int t) {
+      const int64_t kbase = (int64_t)t * kDsBN;
+      if (t + 1 < nkt) {
+        issue_tile<D, kDsBN, 4>(Kp + (kbase + kDsBN) * D, pr.kv_len - kbase - kDsBN, nk);
+        issue_tile_pitched<kDsBN, kDsBM, 4>(Sp + kbase + kDsBN, pr.ds_ld, q_left, ns);
+      }
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
+                          !(has_lo && kbase + kDsBN - 1 < wave_lo);
+      if (active) {
+        // B operand dS^T for key step c: lane holds dS[its query][16c + 8hh + e], e = 0..7
+        bf16x8 dsb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dsb[c] = row_operand(sb, sa, c);
+        const bool edge = (kbase + kDsBN > pr.kv_len) || (diag && kbase + kDsBN - 1 > wq_first) ||
+                          (has_lo && kbase < wave_lo_max);
+        if (edge) {
+          // visible keys of this lane's query, as tile offsets [kmin, kmax]
+          const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
+          const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kDsBN - 1 ? kDsBN - 1 : lim - kbase));
+          const int kmin = has_lo ? (int)(lo - kbase < 0 ? 0 : (lo - kbase > kDsBN ? kDsBN : lo - kbase)) : 0;
+          // element e of step c is key 16 c + 8 hh + e: compare the compile-time part against the
+          // bounds shifted by 8 hh; bf16 element 2 i + b is half b of 32-bit word i
+          const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            u32x4 wv = __builtin_bit_cast(u32x4, dsb[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int k0 = 16 * c + 2 * i;
+              const unsigned lo16 = (k0 >= kml && k0 <= kmh) ? 0xFFFFu : 0u;
+              const unsigned hi16 = (k0 + 1 >= kml && k0 + 1 <= kmh) ? 0xFFFF0000u : 0u;
+              wv[i] &= lo16 | hi16;
+            }
+            dsb[c] = __builtin_bit_cast(bf16x8, wv);
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dq[db] = mfma32(tr_operand(kb, kt, D, c, db), dsb[c], dq[db]);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+
+    if (kt0 >= nkt) continue;  // uniform over the workgroup
+    issue_tile<D, kDsBN, 4>(Kp + kt0 * kDsBN * D, pr.kv_len - kt0 * kDsBN, buf);
+    issue_tile_pitched<kDsBN, kDsBM, 4>(Sp + kt0 * kDsBN, pr.ds_ld, q_left, buf + KT);
+    wait_vmem();
+    __syncthreads();
+    for (int t = (int)kt0; t < nkt; ++t) {
+      u16* cur = buf + ((t - (int)kt0) & 1) * (KT + ST);
+      u16* nxt = buf + ((t - (int)kt0 + 1) & 1) * (KT + ST);
+      step(cur, cur + KT, nxt, nxt + KT, t);
+    }
+  }
+
+  if (qvalid) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh);
+        f32x4 u = *dst;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] += dq[db][4 * j + i];
+        *dst = u;
+      }
+  }
+}
+
+template <int D>
+int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
+  int e;
+  const int64_t nkv = kv.dk ? (int64_t)kv.B * kv.Hq * kv.tiles_per_head : 0;
+  const int64_t nq = q.U ? (int64_t)q.B * q.Hq * q.tiles_per_head : 0;
+  if (nkv > 0) {
+    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
+    if ((e = (int)hipGetLastError())) return e;
+  }
+  if (nq == 0) return 0;
+  // the dQ kernel reads what the dK/dV kernel wrote: with a side stream it starts after it
+  hipStream_t qs = (hipStream_t)stream;
+  if (fork) {
+    if ((e = (int)hipEventRecord((hipEvent_t)fork->fork, (hipStream_t)stream))) return e;
+    if ((e = (int)hipStreamWaitEvent((hipStream_t)fork->side, (hipEvent_t)fork->fork, 0))) return e;
+    qs = (hipStream_t)fork->side;
+  }
+  hipLaunchKernelGGL(chunk_bwd_dq_ds_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, qs, q);
+  if ((e = (int)hipGetLastError())) return e;
+  if (qs != (hipStream_t)stream && fork->join) {
+    if ((e = (int)hipEventRecord((hipEvent_t)fork->join, qs))) return e;
+    if ((e = (int)hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)fork->join, 0))) return e;
+  }
+  return 0;
+}
+
 template <int D>
 int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   int e;
@@ -479,6 +694,10 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
 
 int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   return kv.D == 128 ? launch_bwd<128>(kv, q, stream, fork) : launch_bwd<64>(kv, q, stream, fork);
+}
+
+int launch_chunk_bwd_ds_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
+  return kv.D == 128 ? launch_bwd_ds<128>(kv, q, stream, fork) : launch_bwd_ds<64>(kv, q, stream, fork);
 }
 
 }  // namespace ra

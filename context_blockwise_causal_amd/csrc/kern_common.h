@@ -164,6 +164,11 @@ __device__ __forceinline__ void g2lds16(const void* src, void* dst_wave) {
   __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)dst_wave, 16, 0, 0);
 }
 
+// The same with the non-temporal cache policy, for data read once (streamed past the caches).
+__device__ __forceinline__ void g2lds16_nt(const void* src, void* dst_wave) {
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)dst_wave, 16, 0, 2);
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Issues the loads of a swizzled ROWS x D bf16 tile whose row r comes from global row
@@ -186,6 +191,27 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t va
     const int c = (lane % CH) ^ swz(row, D);
     const unsigned off = (unsigned)((row < last ? row : last) * D + c * 8) * 2u;  // bytes
     g2lds16(reinterpret_cast<const char*>(g) + off, tile + i * 512);
+  }
+}
+
+// The same for a tile whose global rows are `pitch` elements apart (COLS elements used per row),
+// read once: loaded with the non-temporal policy.
+template <int COLS, int ROWS, int NWAVES>
+__device__ __forceinline__ void issue_tile_pitched(const u16* __restrict__ g, int64_t pitch,
+                                                   int64_t valid_rows, u16* tile) {
+  constexpr int CH = COLS / 8;
+  constexpr int RPI = 64 / CH;
+  constexpr int NI = ROWS / RPI;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  static_assert(NI % NWAVES == 0, "tile rows must split evenly over the wavefronts");
+  const int last = (int)(valid_rows < ROWS ? valid_rows : ROWS) - 1;
+#pragma unroll
+  for (int k = 0; k < NI / NWAVES; ++k) {
+    const int i = k * NWAVES + w;
+    const int row = i * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz(row, COLS);
+    const int64_t off = ((int64_t)(row < last ? row : last) * pitch + c * 8) * 2;  // bytes
+    g2lds16_nt(reinterpret_cast<const char*>(g) + off, tile + i * 512);
   }
 }
 

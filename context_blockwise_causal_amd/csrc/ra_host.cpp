@@ -31,6 +31,7 @@ struct ra_context {
   hipEvent_t bfork, bjoin;     // the backward's dQ kernel on a pool stream beside dK/dV
   hipEvent_t qfreed[2];        // the backward ring's dQ kernels have finished reading a slot
   hipEvent_t ajoin;            // the ring's second compute stream has finished
+  hipEvent_t dslocal;          // the backward's local-step dQ kernel has read its dS buffer
 };
 
 namespace ra {
@@ -124,6 +125,35 @@ int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* 
   return kp.nranges ? launch_chunk_bwd_f32(kp, stream) : 0;
 }
 
+// Backward with stored dS (bf16): `ds` holds at least ds_layout(s, pairs, n) bytes.
+int run_bwd_ds(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* ds, void* stream,
+               const BwdFork* fork) {
+  KParams kq = kp;
+  build_ranges(&kp, pairs, n, false, kBwdTileRows);
+  build_ranges(&kq, pairs, n, true, kBwdDsTileRows);
+  ds_layout(s, pairs, n, &kp);
+  ds_layout(s, pairs, n, &kq);
+  kp.ds = ds;
+  kq.ds = ds;
+  return kp.nranges ? launch_chunk_bwd_ds_bf16(kp, kq, stream, fork) : 0;
+}
+
+// The ring's receive on one GPU: owner's K and V chunk, (B, Hkv, S/cp, D) each, copied out of the
+// owner-major ring tensors into `dst` (K then V).
+int stage_copy(const Shape& s, int32_t owner, const void* k_ring, const void* v_ring, void* dst,
+               hipStream_t stream) {
+  const int64_t chunk_bytes = s.chunk * s.D * s.esize;  // one (b, kv head) block of a chunk
+  const int64_t head_bytes = s.S * s.D * s.esize;       // pitch of the ring tensors
+  const int64_t half = s.B * s.Hkv * chunk_bytes;
+  const int64_t off = (int64_t)owner * chunk_bytes;
+  int e;
+  if ((e = launch_copy2d((const char*)k_ring + off, head_bytes, dst, chunk_bytes, chunk_bytes, s.B * s.Hkv,
+                         stream)))
+    return e;
+  return launch_copy2d((const char*)v_ring + off, head_bytes, (char*)dst + half, chunk_bytes, chunk_bytes,
+                       s.B * s.Hkv, stream);
+}
+
 bool any_compute(const ra_pair* pairs, int32_t n) {
   for (int i = 0; i < n; ++i)
     if (pairs[i].mask != RA_MASK_SKIP && pairs[i].q_len > 0 && pairs[i].kv_len > 0) return true;
@@ -142,8 +172,9 @@ int staged_steps(const Shape& s, int32_t rank) {
   return n;
 }
 
-// The ring loop shared by both passes.  `step_fn(stream, kv_k, kv_v, kv_head_rows, owner,
-// pairs, n)` enqueues one step's compute on `stream` and, when `side` is not NULL, part of it on
+// The ring loop shared by both passes.  `step_fn(stream, slot, kv_k, kv_v, kv_head_rows, owner,
+// pairs, n)` (slot -1 for the local step) enqueues one step's compute on `stream` and, when `side`
+// is not NULL, part of it on
 // `side`, which the caller joins after the loop.  With `alt` set, the steps staged in slot 1 run
 // on `alt` instead of the compute stream (only for steps that do not depend on each other); the
 // loop joins `alt` into the compute stream before it returns.  A slot is refilled only once all
@@ -172,7 +203,6 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   }
   const int64_t row_bytes = s.D * s.esize;
   const int64_t chunk_bytes = s.chunk * row_bytes;       // one (b, kv head) block of a chunk
-  const int64_t head_bytes = s.S * row_bytes;            // pitch of the ring tensors
   const int64_t slot_half = s.B * s.Hkv * chunk_bytes;   // K part of a slot; V follows
   char* slots[2] = {slot0, slot1};
   int e;
@@ -182,13 +212,7 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
     if (k >= 2 && (e = (int)hipStreamWaitEvent(ss, ctx->freed[sl], 0))) return dev_err(e, "wait slot_free");
     if (k >= 2 && side && (e = (int)hipStreamWaitEvent(ss, ctx->qfreed[sl], 0)))
       return dev_err(e, "wait slot_free (side)");
-    const int64_t off = (int64_t)staged[k].owner * chunk_bytes;
-    if ((e = launch_copy2d((const char*)k_ring + off, head_bytes, slots[sl], chunk_bytes, chunk_bytes,
-                           s.B * s.Hkv, ss)))
-      return dev_err(e, "staging copy (K)");
-    if ((e = launch_copy2d((const char*)v_ring + off, head_bytes, slots[sl] + slot_half, chunk_bytes,
-                           chunk_bytes, s.B * s.Hkv, ss)))
-      return dev_err(e, "staging copy (V)");
+    if ((e = stage_copy(s, staged[k].owner, k_ring, v_ring, slots[sl], ss))) return dev_err(e, "staging copy");
     if ((e = (int)hipEventRecord(ctx->ready[sl], ss))) return dev_err(e, "record slot_ready");
     return RA_OK;
   };
@@ -207,7 +231,7 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   if (nstaged > 0 && (st = issue_copy(0)) != RA_OK) return st;
   if (have_local) {
     const int64_t off = (int64_t)rank * chunk_bytes;
-    if ((e = step_fn(cs, (const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
+    if ((e = step_fn(cs, -1, (const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
                      local.pairs, local.n)))
       return dev_err(e, "chunk kernel (local step)");
   }
@@ -216,7 +240,7 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
     const int sl = k & 1;
     const hipStream_t t = kvs[sl];
     if ((e = (int)hipStreamWaitEvent(t, ctx->ready[sl], 0))) return dev_err(e, "wait slot_ready");
-    if ((e = step_fn(t, slots[sl], slots[sl] + slot_half, s.chunk, staged[k].owner, staged[k].pairs,
+    if ((e = step_fn(t, sl, slots[sl], slots[sl] + slot_half, s.chunk, staged[k].owner, staged[k].pairs,
                      staged[k].n)))
       return dev_err(e, "chunk kernel (staged step)");
     if ((e = (int)hipEventRecord(ctx->freed[sl], t))) return dev_err(e, "record slot_free");
@@ -248,6 +272,7 @@ void release(ra_context* c) {
     ev(c->qfreed[i]);
   }
   ev(c->ajoin);
+  ev(c->dslocal);
   for (int i = 0; i < kMaxSteps; ++i) ev(c->done[i]);
   ev(c->fin);
   ev(c->bfork);
@@ -282,6 +307,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->qfreed[i], hipEventDisableTiming);
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ajoin, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->dslocal, hipEventDisableTiming);
   for (int i = 0; i < kMaxSteps && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fin, hipEventDisableTiming);
@@ -346,10 +372,23 @@ ra_status ra_ulysses_reshard(ra_context* ctx, const ra_problem* prob, int32_t st
   if (heads != s.Hq && heads != s.Hkv) return fail(RA_ERR_INVALID, "heads must be heads_q or heads_kv");
   if (heads % s.cp) return fail(RA_ERR_INVALID, "heads (%lld) must be divisible by cp_size (%d)", (long long)heads, s.cp);
   if ((st = need_ptrs({src, dst})) != RA_OK) return st;
-  if (src == dst) return fail(RA_ERR_INVALID, "re-shard cannot run in place");
-  if (s.B * heads > 65535) return fail(RA_ERR_UNSUPPORTED, "batch * heads above 65535 in one re-shard");
+  // every re-shard step reads and writes batch * heads * seq_len/cp * head_dim elements
+  const uintptr_t nbytes = (uintptr_t)(s.B * heads * s.chunk * s.D * s.esize);
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + nbytes && b < a + nbytes) return fail(RA_ERR_INVALID, "re-shard src and dst overlap");
   DeviceGuard g(ctx->device);
   return dev_err(launch_reshard(s, step, heads, src, dst, stream), "ulysses re-shard");
+}
+
+ra_status ra_stage_kv(ra_context* ctx, const ra_problem* prob, int32_t owner, const void* k_ring,
+                      const void* v_ring, void* dst, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if ((st = check_rank(s, owner)) != RA_OK) return st;
+  if ((st = need_ptrs({k_ring, v_ring, dst})) != RA_OK) return st;
+  DeviceGuard g(ctx->device);
+  return dev_err(stage_copy(s, owner, k_ring, v_ring, dst, (hipStream_t)stream), "staging copy");
 }
 
 ra_status ra_state_init(ra_context* ctx, const ra_problem* prob, int64_t rows, float* U, float* m,
@@ -443,6 +482,56 @@ ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* prob, const void* q, c
   return dev_err(run_bwd(s, kp, pairs, n_pairs, stream, &fork), "chunk backward");
 }
 
+ra_status ra_chunk_bwd_ds_size(const ra_problem* prob, int64_t q_rows, int64_t kv_rows,
+                               const ra_pair* pairs, int32_t n_pairs, size_t* bytes) {
+  clear_error();
+  Shape s;
+  ra_status st = resolve(prob, &s);
+  if (st != RA_OK) return st;
+  if (!bytes) return fail(RA_ERR_INVALID, "bytes is NULL");
+  if (q_rows < 0 || kv_rows < 0) return fail(RA_ERR_INVALID, "row counts must be >= 0");
+  if ((st = check_pairs(pairs, n_pairs, q_rows, kv_rows)) != RA_OK) return st;
+  *bytes = s.dtype == RA_BF16 ? ds_layout(s, pairs, n_pairs, nullptr) : 0;
+  return RA_OK;
+}
+
+ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* prob, const void* q, const void* dO,
+                          const float* lse, const float* delta, int64_t q_rows, const void* k,
+                          const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
+                          float* dq_acc, float* dk_acc, float* dv_acc, void* scratch,
+                          size_t scratch_bytes, void* stream) {
+  Shape s;
+  ra_status st = common(ctx, prob, &s);
+  if (st != RA_OK) return st;
+  if (q_rows < 0 || kv_rows < 0) return fail(RA_ERR_INVALID, "row counts must be >= 0");
+  if ((st = check_pairs(pairs, n_pairs, q_rows, kv_rows)) != RA_OK) return st;
+  if ((st = need_ptrs({q, dO, lse, delta, k, v})) != RA_OK) return st;
+  if ((dk_acc == nullptr) != (dv_acc == nullptr))
+    return fail(RA_ERR_INVALID, "dk_acc and dv_acc must both be given or both be NULL");
+  if (!dq_acc && !dk_acc) return fail(RA_ERR_INVALID, "no gradient requested (dq_acc, dk_acc, dv_acc all NULL)");
+  if (dq_acc && (st = need_ptrs({dq_acc})) != RA_OK) return st;
+  if (dk_acc && (st = need_ptrs({dk_acc, dv_acc})) != RA_OK) return st;
+  KParams kp = base_params(s);
+  kp.q = q; kp.dO = dO; kp.lse = lse; kp.delta = delta; kp.k = k; kp.v = v;
+  kp.U = dq_acc; kp.dk = dk_acc; kp.dv = dv_acc;
+  kp.q_head_rows = q_rows;
+  kp.kv_head_rows = kv_rows;
+  kp.dkv_head_rows = kv_rows;
+  if (s.dtype != RA_BF16) {  // the fp32 path forms dQ in its single kernel: no scratch
+    if (!dq_acc || !dk_acc)
+      return fail(RA_ERR_UNSUPPORTED, "the fp32 path computes all three gradients in one pass");
+    DeviceGuard g(ctx->device);
+    return dev_err(run_bwd(s, kp, pairs, n_pairs, stream, nullptr), "chunk backward");
+  }
+  const size_t need = ds_layout(s, pairs, n_pairs, nullptr);
+  if (need > 0 && (!scratch || !aligned16(scratch)))
+    return fail(RA_ERR_INVALID, "scratch is NULL or not 16-byte aligned");
+  if (scratch_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, need);
+  DeviceGuard g(ctx->device);
+  return dev_err(run_bwd_ds(s, kp, pairs, n_pairs, scratch, stream, nullptr), "chunk backward (stored dS)");
+}
+
 ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* prob, int64_t n, const float* src,
                            void* dst, void* stream) {
   Shape s;
@@ -495,9 +584,10 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   kp.q = q_slice;
   kp.q_head_rows = s.chunk;
   bool first = true;
-  auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
-                  const ra_pair* pairs, int32_t n) -> int {
+  auto step = [&](hipStream_t t, int slot, const void* k, const void* v, int64_t kv_head_rows,
+                  int32_t owner, const ra_pair* pairs, int32_t n) -> int {
     (void)owner;
+    (void)slot;
     const bool b = t != cs;  // slot-1 steps run on the second stream
     kp.U = b ? U2 : U; kp.m = b ? m2 : m; kp.l = b ? l2 : l;
     kp.fresh = first ? 1 : 0;
@@ -641,8 +731,15 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
   const int64_t pitch = s.S * s.D;    // head stride of the ring-ordered tensors
   const int64_t nkvh = s.B * s.Hkv;
   bool visited[64] = {};
-  auto step = [&](hipStream_t t, const void* k, const void* v, int64_t kv_head_rows, int32_t owner,
-                  const ra_pair* pairs, int32_t n) -> int {
+  // bf16: the dK/dV kernel stores dS into one of two buffers (the local step and the steps staged
+  // in slot 1 use buffer 1, slot-0 steps buffer 0) and the step's dQ kernel reads it on `side`.
+  // A staged step's buffer is free once the dQ kernel two steps back has run: its staging copy
+  // already waited for that (the slot's side event).  The local step shares buffer 1 with the
+  // first slot-1 step, which waits for the local dQ kernel explicitly.
+  const bool use_ds = s.dtype == RA_BF16 && W.ds_bytes > 0;
+  bool local_recorded = false, local_waited = false;
+  auto step = [&](hipStream_t t, int slot, const void* k, const void* v, int64_t kv_head_rows,
+                  int32_t owner, const ra_pair* pairs, int32_t n) -> int {
     kp.k = k; kp.v = v;
     kp.kv_head_rows = kv_head_rows;
     float* const dko = dk + (int64_t)owner * blk;
@@ -652,7 +749,20 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     if ((r = launch_zero2d(dvo, pitch * 4, blk * 4, nkvh, t))) return r;
     kp.dk = dko;
     kp.dv = dvo;
-    if ((r = run_bwd(s, kp, pairs, n, t, &fork))) return r;
+    if (use_ds) {
+      const int buf = slot == 0 ? 0 : 1;
+      if (slot == 1 && local_recorded && !local_waited) {
+        if ((r = (int)hipStreamWaitEvent(t, ctx->dslocal, 0))) return r;
+        local_waited = true;
+      }
+      if ((r = run_bwd_ds(s, kp, pairs, n, ws + W.ds[buf], t, &fork))) return r;
+      if (slot < 0) {
+        if ((r = (int)hipEventRecord(ctx->dslocal, side))) return r;
+        local_recorded = true;
+      }
+    } else if ((r = run_bwd(s, kp, pairs, n, t, &fork))) {
+      return r;
+    }
     visited[owner] = true;
     const int64_t off = (int64_t)owner * blk * s.esize;
     if ((r = launch_cast2d(dko, static_cast<char*>(dk_ring) + off, pitch, blk, nkvh, s.dtype, t))) return r;

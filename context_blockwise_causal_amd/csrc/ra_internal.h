@@ -47,7 +47,7 @@ int64_t slice_chunk(const Shape& s, int32_t rank, int32_t which);
 // staged in slot 1, merged into the first after the ring (two states let consecutive steps run
 // concurrently); then the slots.
 struct FwdWs { size_t U, m, l, U2, m2, l2, slot[2], total; bool two; };
-struct BwdWs { size_t dq, dk, dv, delta, slot[2], total; };
+struct BwdWs { size_t dq, dk, dv, delta, slot[2], ds[2], ds_bytes, total; };
 FwdWs fwd_ws(const Shape& s);
 // Split-KV forward: the running state, then one partial state per ring step (cp of them).
 struct SplitWs { size_t U, m, l, part, part_stride, total; };
@@ -70,6 +70,10 @@ struct KPair {
   int64_t q_row0, kv_row0, q_len, kv_len;
   int32_t mask, pad_;
   int64_t q_pos0, kv_pos0;  // sequence positions of the first query / key row
+  // Backward with stored dS: the pair's dS block starts ds_off elements into KParams::ds; it
+  // holds, per (batch, query head), q_len rows (queries) of ds_ld elements (keys, ds_ld a
+  // multiple of 128 >= kv_len).
+  int64_t ds_off, ds_ld;
 };
 
 struct KParams {
@@ -84,6 +88,7 @@ struct KParams {
   float* l;
   float* dk;  // bwd accumulators
   float* dv;
+  void* ds;   // bwd: bf16 dS scratch (see KPair::ds_off); NULL = not stored
   int64_t q_head_rows;    // head stride (rows) of q, dO, U, m, l, lse, delta, dq
   int64_t kv_head_rows;   // head stride (rows) of k, v
   int64_t dkv_head_rows;  // head stride (rows) of dk, dv
@@ -102,6 +107,15 @@ struct KParams {
 // Builds the range table: groups non-SKIP pairs by their outer range and assigns tiles of
 // `tile_rows` rows.  by_q selects the forward grouping (Q ranges) or the backward (K/V).
 void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64_t tile_rows);
+// Lays out the stored-dS scratch of a pair list (bytes; 0 when no pair computes) and, when kp is
+// given, fills the pairs' ds_off / ds_ld (call after build_ranges).  Each non-SKIP pair gets
+// B * Hq * q_len * ds_ld bf16 values, ds_ld = kv_len rounded up to 128, blocks 256-byte aligned.
+size_t ds_layout(const Shape& s, const ra_pair* pairs, int32_t n, KParams* kp);
+// Largest ds_layout over the ring steps of a rank view (the size of one dS buffer).
+size_t ds_step_max(const Shape& s, int32_t rank);
+// Above this size per step the rank-view backward recomputes S and dP for dQ instead of storing
+// dS (the Qwen3-shaped single-chunk share would need 34 GB).
+constexpr size_t kDsCap = (size_t)8 << 30;
 
 // Lowest key position visible to query position t under the window / chunk restrictions
 // (INT64_MIN when neither is set); the causal bound is key <= t.  constexpr: usable on the
@@ -136,11 +150,16 @@ int launch_chunk_fwd_bf16(const KParams& kp, void* stream);
 // for it through `join`; with join == nullptr it does not, and the caller joins later.
 struct BwdFork { void* side; void* fork; void* join; };
 int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
+// Backward with stored dS: the dK/dV kernel (kv.ds set) writes dS^T, then the dQ kernel reads it
+// (q.ds set, Q-major ranges): dq += dS K.  With `fork` the dQ kernel runs on `side` after the
+// dK/dV kernel (fork event recorded after it), joined into `stream` when fork->join is set.
+int launch_chunk_bwd_ds_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
 constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)
 constexpr int64_t kBwdTileRows = 128;   // K/V rows per dK/dV workgroup (bf16 MFMA kernel)
 constexpr int64_t kBwdQTileRows = 128;  // Q rows per dQ workgroup (bf16 MFMA kernel)
+constexpr int64_t kBwdDsTileRows = 128; // Q rows per workgroup of the dQ-from-stored-dS kernel
 constexpr int64_t kF32FwdTileRows = 1;  // one row per workgroup in the fp32 path
 constexpr int64_t kF32BwdTileRows = 1;
 

@@ -54,6 +54,10 @@ ra_status resolve(const ra_problem* p, Shape* out) {
   // 32-bit grid indices.
   const int64_t rows = p->batch * p->heads_q * (p->seq_len / p->cp_size);
   if (rows > (int64_t(1) << 40)) return fail(RA_ERR_UNSUPPORTED, "problem too large");
+  // The row-wise kernels (layout, staging copy, re-shard) put one (batch, head) per grid row,
+  // and a grid's y dimension holds at most 65535.
+  if (p->batch * p->heads_q > 65535)
+    return fail(RA_ERR_UNSUPPORTED, "batch * heads_q (%lld) above 65535", (long long)(p->batch * p->heads_q));
   Shape s;
   s.B = p->batch;
   s.S = p->seq_len;
@@ -205,6 +209,33 @@ SplitWs split_ws(const Shape& s) {
   return w;
 }
 
+size_t ds_layout(const Shape& s, const ra_pair* pairs, int32_t n, KParams* kp) {
+  size_t off = 0;  // elements
+  for (int i = 0; i < n; ++i) {
+    const ra_pair& p = pairs[i];
+    if (p.mask == RA_MASK_SKIP || p.q_len == 0 || p.kv_len == 0) continue;
+    const int64_t ld = (p.kv_len + 127) / 128 * 128;
+    if (kp) {
+      kp->pairs[i].ds_off = (int64_t)off;
+      kp->pairs[i].ds_ld = ld;
+    }
+    off += align256((size_t)(s.B * s.Hq * p.q_len * ld) * 2) / 2;
+  }
+  return off * 2;
+}
+
+size_t ds_step_max(const Shape& s, int32_t rank) {
+  size_t mx = 0;
+  for (int32_t i = 0; i < s.cp; ++i) {
+    int32_t owner, n;
+    ra_pair pairs[4];
+    plan_step(s, rank, i, &owner, pairs, &n);
+    const size_t b = ds_layout(s, pairs, n, nullptr);
+    mx = b > mx ? b : mx;
+  }
+  return mx;
+}
+
 BwdWs bwd_ws(const Shape& s) {
   BwdWs w;
   const size_t rows = (size_t)(s.B * s.Hq * s.chunk);
@@ -220,6 +251,21 @@ BwdWs bwd_ws(const Shape& s) {
     w.slot[i] = off;
     if (i < nslots) off += align256(slot);
   }
+  // Two dS buffers for the bf16 path: a step's dQ kernel reads its buffer while the next step's
+  // dK/dV kernel fills the other.  The largest step over all ranks sizes them, so that the
+  // workspace size does not depend on the rank.
+  w.ds_bytes = 0;
+  if (s.dtype == RA_BF16) {
+    for (int32_t r = 0; r < s.cp; ++r) {
+      const size_t b = ds_step_max(s, r);
+      w.ds_bytes = b > w.ds_bytes ? b : w.ds_bytes;
+    }
+    if (w.ds_bytes > kDsCap) w.ds_bytes = 0;  // recompute path
+  }
+  for (int i = 0; i < 2; ++i) {
+    w.ds[i] = off;
+    off += align256(w.ds_bytes);
+  }
   w.total = off;
   return w;
 }
@@ -230,7 +276,7 @@ void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64
   int nr = 0;
   for (int i = 0; i < n; ++i) {
     const ra_pair& p = pairs[i];
-    kp->pairs[i] = KPair{p.q_row0, p.kv_row0, p.q_len, p.kv_len, p.mask, 0, p.q_pos0, p.kv_pos0};
+    kp->pairs[i] = KPair{p.q_row0, p.kv_row0, p.q_len, p.kv_len, p.mask, 0, p.q_pos0, p.kv_pos0, 0, 0};
     if (p.mask == RA_MASK_SKIP || p.q_len == 0 || p.kv_len == 0) continue;
     const int64_t r0 = by_q ? p.q_row0 : p.kv_row0;
     const int64_t rl = by_q ? p.q_len : p.kv_len;

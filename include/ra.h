@@ -105,9 +105,15 @@ const char* ra_status_str(int32_t status);
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* ra_last_error(void);
 
-/* Checks the problem and a rank: heads_q % heads_kv == 0, seq_len % cp_size == 0 (and
- * % (2*cp_size) for zigzag), 0 <= rank < cp_size, positive sizes, a known dtype/layout.
- * head_dim outside {64,128} returns RA_ERR_UNSUPPORTED. */
+/* Checks the problem and a rank against the scope the pages fix: fixed-length, equally split,
+ * causal self-attention ("Feat: Context Parallel", section 实现边界), MHA or GQA with
+ * n_rep = heads_q / heads_kv ("Feat: Context Parallel", review thread on the attention helper),
+ * zigzag splitting into 2 * cp_size chunks ("上下文并行", Zig-Zag Ring Attention).  So:
+ * heads_q % heads_kv == 0, seq_len % cp_size == 0 (and % (2*cp_size) for zigzag),
+ * 0 <= rank < cp_size, positive sizes, a known dtype/layout, finite scale >= 0, window and
+ * attn_chunk >= 0: RA_ERR_INVALID otherwise.  head_dim outside {64,128} and
+ * batch * heads_q > 65535 return RA_ERR_UNSUPPORTED.  Every entry point that takes a problem
+ * applies these checks first. */
 ra_status ra_validate(const ra_problem* problem, int32_t rank);
 
 /* Ring step plan ("上下文并行", "朴素 Ring Attention": each round a rank sends its K/V to the
@@ -161,7 +167,8 @@ ra_status ra_layout_scatter(ra_context* ctx, const ra_problem* problem, int32_t 
  * RA_A2A_SEQ_UNPACK:  receive buffer (block j = heads of rank j) -> sequence shard
  * The all-to-all itself (receive block j on rank r = send block r of rank j) is the
  * collective and not part of this library.  A pure permutation: bit-exact.  src and dst must
- * not overlap; RA_ERR_INVALID otherwise, for an unknown step, or heads not divisible by cp. */
+ * not overlap (each spans batch * heads * seq_len/cp * head_dim elements); RA_ERR_INVALID
+ * otherwise, for an unknown step, or heads not divisible by cp. */
 typedef enum {
   RA_A2A_SEQ_PACK = 0,
   RA_A2A_HEAD_UNPACK = 1,
@@ -172,6 +179,15 @@ typedef enum {
 ra_status ra_ulysses_reshard(ra_context* ctx, const ra_problem* problem, int32_t step,
                              int64_t heads, const void* src, void* dst, void* stream);
 
+/* The ring's receive on one GPU ("上下文并行", 朴素 Ring Attention: each step a rank receives
+ * the previous rank's K/V chunk; "Feat: Context Parallel" 主要改动: a separate stream carries
+ * it): copies owner `owner`'s K and V chunk, (batch, heads_kv, seq_len/cp, head_dim) each, out
+ * of the owner-major ring tensors k_ring / v_ring (batch, heads_kv, seq_len, head_dim) into
+ * `dst`, K first, then V.  The rank views stage every chunk but their own this way.  Bit-exact.
+ * RA_ERR_INVALID for an owner outside [0, cp_size) or NULL / misaligned pointers. */
+ra_status ra_stage_kv(ra_context* ctx, const ra_problem* problem, int32_t owner,
+                      const void* k_ring, const void* v_ring, void* dst, void* stream);
+
 /* Empty online-softmax state for (batch, heads_q, rows): U = 0, m = -inf, l = 0. */
 ra_status ra_state_init(ra_context* ctx, const ra_problem* problem, int64_t rows, float* U,
                         float* m, float* l, void* stream);
@@ -179,9 +195,12 @@ ra_status ra_state_init(ra_context* ctx, const ra_problem* problem, int64_t rows
 /* Chunk forward ("上下文并行", "朴素 Ring Attention": safe softmax and the
  * FlashAttention-2-style update of the output, row max and row sum per K/V block).
  * q: (batch, heads_q, q_rows, head_dim); k, v: (batch, heads_kv, kv_rows, head_dim).
- * State (fp32, in/out): U (batch, heads_q, q_rows, head_dim) unnormalised output,
- * m (batch, heads_q, q_rows) row max of the scaled scores (natural-log units),
- * l (batch, heads_q, q_rows) row sum of exp(score - m).
+ * State (fp32, in/out): m (batch, heads_q, q_rows) is the row's reference point (natural-log
+ * units), l (batch, heads_q, q_rows) the row sum of exp(score - m) and U (batch, heads_q,
+ * q_rows, head_dim) the unnormalised output sum of exp(score - m) v, so m + ln l is the row's
+ * log-sum-exp and U / l its output.  m is at least the row max minus 8 ln 2: the bf16 kernel
+ * moves m only when a key block's max exceeds it by more than 8 ln 2 (so exp(score - m) <= 256),
+ * which skips most rescales of U; the empty state is (U = 0, m = -inf, l = 0).
  * Every non-SKIP pair is folded into its rows exactly once; pairs may share Q rows, but the
  * Q ranges of two pairs must be identical or disjoint.  Rows no pair touches, and SKIP
  * pairs, leave the state bit-unchanged.  bf16 path: Q K^T and P V on bf16 MFMA with fp32
@@ -206,7 +225,12 @@ ra_status ra_fwd_finalize(ra_context* ctx, const ra_problem* problem, int64_t ro
                           const float* U, const float* m, const float* l, void* o, float* lse,
                           void* stream);
 
-/* delta = rowsum(dO * O) in fp32, (batch, heads_q, rows): the backward's per-row term. */
+/* Backward pre-pass: delta = rowsum(dO * O) in fp32, (batch, heads_q, rows).  The p2p backward
+ * recomputes the probabilities from the saved log-sum-exp ("Feat: Context Parallel", 主要改动);
+ * the gradient of the softmax then needs, per query row, the inner product of the row's output
+ * and output gradient, which this computes once for all ring steps.  o and dO: (batch, heads_q,
+ * rows, head_dim) in problem->dtype; delta: caller-owned fp32 device memory, overwritten.
+ * RA_ERR_INVALID for NULL or misaligned pointers or rows < 0. */
 ra_status ra_bwd_preprocess(ra_context* ctx, const ra_problem* problem, int64_t rows,
                             const void* o, const void* dO, float* delta, void* stream);
 
@@ -224,6 +248,29 @@ ra_status ra_chunk_bwd(ra_context* ctx, const ra_problem* problem, const void* q
                        const float* lse, const float* delta, int64_t q_rows, const void* k,
                        const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
                        float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
+
+/* Chunk backward with stored dS: the same gradients as ra_chunk_bwd (all three required), formed
+ * by five contractions instead of seven.  The dK/dV kernel, which forms dS = P (dP - delta) for
+ * its dK contraction anyway, also writes scale * dS (bf16, the very operand of that contraction)
+ * into `scratch`; a second kernel then forms dQ += (scale dS) K as a plain contraction that
+ * streams the stored dS, instead of recomputing S and dP per query row ("Feat: Context
+ * Parallel" 主要改动: the p2p backward recomputes P from the saved log-sum-exp once per chunk
+ * pair).  Arguments as for ra_chunk_bwd, plus `scratch`: caller-owned device memory of at least
+ * ra_chunk_bwd_ds_size bytes (16-byte aligned; its contents on entry do not matter; it must not
+ * be reused by other work until this call's work has finished on `stream`).  The two kernels can
+ * be run as two calls: dq_acc = NULL runs only the first (dK, dV, and dS into the scratch);
+ * dk_acc = dv_acc = NULL runs only the second, which reads the scratch a first-phase call with
+ * the same arguments filled.  For fp32 problems the scratch is not used (size 0) and the call
+ * runs the fp32 backward, which needs all three gradients (RA_ERR_UNSUPPORTED otherwise).
+ * RA_ERR_WORKSPACE if scratch_bytes is too small; RA_ERR_INVALID for NULL or misaligned
+ * pointers, only one of dk_acc / dv_acc, no gradient at all, or a bad pair list. */
+ra_status ra_chunk_bwd_ds_size(const ra_problem* problem, int64_t q_rows, int64_t kv_rows,
+                               const ra_pair* pairs, int32_t n_pairs, size_t* bytes);
+ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* problem, const void* q,
+                          const void* dO, const float* lse, const float* delta, int64_t q_rows,
+                          const void* k, const void* v, int64_t kv_rows, const ra_pair* pairs,
+                          int32_t n_pairs, float* dq_acc, float* dk_acc, float* dv_acc,
+                          void* scratch, size_t scratch_bytes, void* stream);
 
 /* Casts n fp32 values to problem->dtype (round to nearest even for bf16): the backward's
  * final step for dQ / dK / dV accumulators. */

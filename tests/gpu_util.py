@@ -12,12 +12,7 @@ BF16_ATOL, BF16_RTOL, BF16_L2 = 2e-2, 1e-2, 1e-2
 F32_ATOL = 1e-5
 
 
-def to_dev(store_array, dtype: str, device="cuda"):
-    """Store-form numpy array (float32, or bf16 bit patterns) -> device tensor, bits unchanged."""
-    if dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(store_array).view(np.int16))
-        return t.to(device).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(store_array, dtype=np.float32)).to(device)
+to_dev = api.to_device
 
 
 def to_f64(t) -> np.ndarray:
@@ -60,3 +55,49 @@ def round_like(x64: np.ndarray, dtype: str) -> np.ndarray:
 
 def problem_for(B, S, Hq, Hkv, D, cp, layout, dtype):
     return api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype)
+
+
+
+def _parallel_blocks(fn, n, block):
+    """fn(row slice) over blocks of rows in parallel threads, one BLAS thread each."""
+    import concurrent.futures
+    import os
+
+    from threadpoolctl import threadpool_limits
+
+    starts = list(range(0, n, block))
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(starts)))
+
+    def one(s):
+        with threadpool_limits(1):
+            return fn(slice(s, s + block))
+
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(one, starts))
+
+
+def oracle_fwd_rows(q, k, v, rows, kpos, block=256, **kw):
+    """O.attention_rows over blocks of query rows in parallel (rows are independent, so this
+    only splits the work): returns O and LSE for all rows."""
+    from oracle import attn64 as O
+    parts = _parallel_blocks(lambda sl: O.attention_rows(q[:, :, sl], k, v, rows[sl], kpos, **kw),
+                             len(rows), block)
+    return np.concatenate([p_[0] for p_ in parts], axis=2), np.concatenate([p_[1] for p_ in parts], axis=2)
+
+
+def oracle_dq_rows(q, k, v, do, rows, kpos, block=128, **kw):
+    """dQ of the given rows from O.attention_rows_bwd, over blocks of rows in parallel."""
+    from oracle import attn64 as O
+    parts = _parallel_blocks(
+        lambda sl: O.attention_rows_bwd(q[:, :, sl], k, v, do[:, :, sl], rows[sl], kpos, **kw)[0],
+        len(rows), block)
+    return np.concatenate(parts, axis=2)
+
+
+def stratified_rows(n, tile, per_tile, rng):
+    """Row sample hitting every `tile`-row tile `per_tile` times (plus the first and last row)."""
+    picks = [0, n - 1]
+    for t0 in range(0, n, tile):
+        m = min(tile, n - t0)
+        picks.extend(t0 + rng.choice(m, min(per_tile, m), replace=False))
+    return np.unique(np.asarray(picks, np.int64))

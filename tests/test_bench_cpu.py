@@ -45,20 +45,26 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
                 w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
         return str(d)
     calib = 1 << 20
+    stage = 1 << 16
     fdir = write("f", "FETCH_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 2),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 100.0),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 300.0)])
+                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 300.0),
+                                     ("ra::copy2d_kernel(...)", stage / 1024 / 3)])
     wdir = write("w", "WRITE_SIZE", [("ra::layout_kernel(...)", calib / 1024),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0)])
+                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
+                                     ("ra::copy2d_kernel(...)", stage / 1024 / 1.5)])
     out = tmp_path / "rec.json"
     monkeypatch.setattr(bench, "traffic_path", lambda name: str(out))
-    bench.traffic_summary("wl", fdir, wdir, calib)
+    bench.traffic_summary("wl", fdir, wdir, calib, stage)
     rec = json.load(open(out))
     k = rec["kernels"]["chunk_bwd_kv_kernel"]
     assert k["fetch_bytes_per_launch"] == pytest.approx(200.0 * 1024 * 2)
     assert k["write_bytes_per_launch"] == pytest.approx(50.0 * 1024)
     assert rec["source_hash"] == bench.source_hash()
+    # the second calibration copy's factors are recorded beside the first
+    assert rec["check"]["fetch_scale"] == pytest.approx(3.0)
+    assert rec["check"]["write_scale"] == pytest.approx(1.5)
 
 
 @pytest.mark.parametrize("window,chunk", [(0, 0), (5, 0), (0, 8), (7, 12), (1, 0)])

@@ -1,5 +1,6 @@
 """GPU parity of the individual C-ABI entry points against the FP64 oracle (and exact numpy
 definitions for the byte-moving kernels).  Sizes span several tiles and end in ragged tails."""
+import itertools
 import math
 
 import numpy as np
@@ -242,9 +243,23 @@ def oracle_stats(q64, k64, v64, do64, qp, kp):
     return o, lse, np.sum(do64 * o, axis=-1)
 
 
+def chunk_bwd(entry, ctx, prob, q, do, lse, delta, k, v, pairs, dq, dk, dv):
+    """The chunk backward through one of its two entry points: "recompute" (ra_chunk_bwd: the dQ
+    kernel recomputes S and dP) or "stored" (ra_chunk_bwd_ds: dQ from the dS the dK/dV kernel
+    stored).  The stored path's scratch starts filled with NaN bit patterns, so that an entry
+    the dQ pass reads without the dK/dV kernel having written it shows up as non-finite."""
+    if entry == "recompute":
+        return api.ra_chunk_bwd(ctx, prob, q, do, lse, delta, k, v, pairs, dq, dk, dv)
+    n = api.ra_chunk_bwd_ds_size(prob, q.shape[2], k.shape[2], pairs)
+    scratch = torch.full((max(16, n),), 0xFF, dtype=torch.uint8, device="cuda")
+    api.ra_chunk_bwd_ds(ctx, prob, q, do, lse, delta, k, v, pairs, dq, dk, dv, scratch)
+    return scratch
+
+
+@pytest.mark.parametrize("entry", ["recompute", "stored"])
 @pytest.mark.parametrize("D,Hq,Hkv,dtype", CASES)
 @pytest.mark.parametrize("kind", ["FULL", "DIAG"])
-def test_chunk_bwd_single_pair(ctx, D, Hq, Hkv, dtype, kind):
+def test_chunk_bwd_single_pair(ctx, D, Hq, Hkv, dtype, kind, entry):
     B = 1 if dtype == "f32" else 2
     qlen = 200 if kind == "DIAG" else 190
     kvlen = 200 if kind == "DIAG" else 300
@@ -264,15 +279,16 @@ def test_chunk_bwd_single_pair(ctx, D, Hq, Hkv, dtype, kind):
     dk = torch.zeros(B, Hkv, kvlen, D, device="cuda")
     dv = torch.zeros_like(dk)
     mask = {"FULL": L.RA_MASK_FULL, "DIAG": L.RA_MASK_DIAG}[kind]
-    api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, [(0, 0, qlen, kvlen, mask)], dq, dk, dv)
+    chunk_bwd(entry, ctx, prob, q, do, lse_d, dl_d, k, v, [(0, 0, qlen, kvlen, mask)], dq, dk, dv)
     torch.cuda.synchronize()
     rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, qp, kp)
     for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
         assert_close(to_f64(got), ref, dtype, name)
 
 
+@pytest.mark.parametrize("entry", ["recompute", "stored"])
 @pytest.mark.parametrize("D,Hq,Hkv,dtype", CASES[:2])
-def test_chunk_bwd_zigzag_local_step_accumulates(ctx, D, Hq, Hkv, dtype):
+def test_chunk_bwd_zigzag_local_step_accumulates(ctx, D, Hq, Hkv, dtype, entry):
     """Step-0 pairs share K/V rows; accumulators are added to, not overwritten."""
     B, L_ = 1, 200
     prob = api.Problem(B, 4 * L_, Hq, Hkv, D, 1, "contiguous", dtype)
@@ -288,8 +304,8 @@ def test_chunk_bwd_zigzag_local_step_accumulates(ctx, D, Hq, Hkv, dtype):
     rng = np.random.default_rng(75)
     base = [rng.standard_normal(s) for s in ((B, Hq, 2 * L_, D), (B, Hkv, 2 * L_, D), (B, Hkv, 2 * L_, D))]
     dq, dk, dv = (torch.tensor(b, dtype=torch.float32, device="cuda") for b in base)
-    api.ra_chunk_bwd(ctx, prob, q, do, torch.tensor(lse, dtype=torch.float32, device="cuda"),
-                     torch.tensor(delta, dtype=torch.float32, device="cuda"), k, v, pairs0, dq, dk, dv)
+    chunk_bwd(entry, ctx, prob, q, do, torch.tensor(lse, dtype=torch.float32, device="cuda"),
+              torch.tensor(delta, dtype=torch.float32, device="cuda"), k, v, pairs0, dq, dk, dv)
     torch.cuda.synchronize()
     rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, pos, pos)
     f32 = lambda a: np.asarray(a, np.float32).astype(np.float64)
@@ -326,3 +342,141 @@ def test_chunk_bwd_partial_gradients(ctx, D, Hq, Hkv, dtype):
         api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq, dk, None)
     with pytest.raises(ValueError):
         api.ra_chunk_bwd(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, None, None, None)
+    if dtype != "bf16":
+        return
+    # the stored-dS entry point as two calls: dK/dV (storing dS), then dQ from the stored dS
+    dk2 = torch.zeros_like(dk)
+    dv2 = torch.zeros_like(dv)
+    dq2 = torch.zeros_like(dq)
+    n = api.ra_chunk_bwd_ds_size(prob, qlen, kvlen, pairs)
+    scratch = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    api.ra_chunk_bwd_ds(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, None, dk2, dv2, scratch)
+    assert torch.count_nonzero(dq2) == 0
+    api.ra_chunk_bwd_ds(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq2, None, None, scratch)
+    torch.cuda.synchronize()
+    for got, ref, name in ((dq2, rdq, "dQ"), (dk2, rdk, "dK"), (dv2, rdv, "dV")):
+        assert_close(to_f64(got), ref, dtype, name + " (stored dS, two calls)")
+    with pytest.raises(ValueError):
+        api.ra_chunk_bwd_ds(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq2, dk2, None, scratch)
+    with pytest.raises(ValueError):  # scratch too small: RA_ERR_WORKSPACE
+        api.ra_chunk_bwd_ds(ctx, prob, q, do, lse_d, dl_d, k, v, pairs, dq2, dk2, dv2, scratch[:n - 256])
+
+
+# ----------------------------------------------------------------------------- merge order
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout,cp", [("contiguous", 2), ("contiguous", 3), ("contiguous", 4),
+                                       ("zigzag", 2), ("zigzag", 4)])
+def test_lse_merge_of_chunk_partials_in_every_order(ctx, dtype, layout, cp):
+    """The online merge does not depend on the order of the chunks ("上下文并行", 朴素 Ring
+    Attention: the (Q, K_j, V_j) blocks may be folded in any order).  The per-owner partials
+    (O_p, LSE_p) of a rank view come from the oracle (attention of the rank's rows against one
+    owner's chunk, empty rows LSE = -inf); ra_lse_merge folds them into an empty state in every
+    order of the owners (cp! orders), and the finalized result must match the oracle's full
+    attention to the stated tolerance each time."""
+    B, Hq, Hkv, D = 1, 4, 2, 64
+    chunk = 48 if layout == "zigzag" else 40
+    S = chunk * cp
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype)
+    q64, k64, v64 = (to_f64(to_dev(rand_store(sh, dtype, 90 + i), dtype)) for i, sh in
+                     enumerate(((B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D))))
+    rank = cp - 1  # the last rank sees every owner's chunk
+    pos = O.rank_positions(S, cp, layout, rank)
+    ro, rl = O.attention_rows(q64[:, :, pos], k64, v64, pos, np.arange(S))
+    parts = []
+    for owner in range(cp):
+        kp = O.rank_positions(S, cp, layout, owner)
+        op, lp = O.attention_rows(q64[:, :, pos], k64[:, :, kp], v64[:, :, kp], pos, kp)
+        parts.append((torch.tensor(op, dtype=torch.float32, device="cuda"),
+                      torch.tensor(lp, dtype=torch.float32, device="cuda")))
+    rows = len(pos)
+    for order in itertools.permutations(range(cp)):
+        U, m, l = api.new_state(prob, rows)
+        api.ra_state_init(ctx, prob, U, m, l)
+        for o_ in order:
+            api.ra_lse_merge(ctx, prob, parts[o_][0], parts[o_][1], U, m, l)
+        o, lse = api.ra_fwd_finalize(ctx, prob, U, m, l)
+        torch.cuda.synchronize()
+        assert_close(to_f64(o), ro, dtype, f"O order {order}")
+        assert np.max(np.abs(to_f64(lse) - rl)) < 1e-5, order
+
+
+@pytest.mark.parametrize("layout,cp", [("contiguous", 4), ("zigzag", 3)])
+def test_gpu_chunk_partials_merge_in_every_order(ctx, layout, cp):
+    """The same with partials the GPU computes: every ring step of a rank view folded by
+    ra_chunk_fwd into its own empty state and finalized (fp32, so O_p is not rounded), then
+    merged in every order of the steps."""
+    B, Hq, Hkv, D, dtype = 1, 2, 1, 64, "f32"
+    chunk = 40
+    S = chunk * cp
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype)
+    stores = [rand_store(sh, dtype, 70 + i) for i, sh in
+              enumerate(((B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D)))]
+    q, k, v = (to_dev(s_, dtype) for s_ in stores)
+    q64, k64, v64 = (to_f64(x) for x in (q, k, v))
+    rank = cp - 1
+    q_sl = api.ra_layout_gather(ctx, prob, rank, 1, q)
+    k_ring = api.ra_layout_gather(ctx, prob, 0, cp, k)
+    v_ring = api.ra_layout_gather(ctx, prob, 0, cp, v)
+    rows = prob.chunk
+    parts = []
+    for i in range(cp):
+        owner, pairs = api.ra_plan_step(prob, rank, i)
+        kc = k_ring[:, :, owner * rows:(owner + 1) * rows].contiguous()
+        vc = v_ring[:, :, owner * rows:(owner + 1) * rows].contiguous()
+        U, m, l = api.new_state(prob, rows)
+        api.ra_state_init(ctx, prob, U, m, l)
+        api.ra_chunk_fwd(ctx, prob, q_sl, kc, vc, pairs, U, m, l)
+        parts.append(api.ra_fwd_finalize(ctx, prob, U, m, l))
+    ro, rl = O.rank_view_fwd(q64, k64, v64, cp, layout, rank)
+    for order in itertools.permutations(range(cp)):
+        U, m, l = api.new_state(prob, rows)
+        api.ra_state_init(ctx, prob, U, m, l)
+        for i in order:
+            api.ra_lse_merge(ctx, prob, parts[i][0], parts[i][1], U, m, l)
+        o, lse = api.ra_fwd_finalize(ctx, prob, U, m, l)
+        torch.cuda.synchronize()
+        assert_close(to_f64(o), ro, dtype, f"O order {order}")
+        assert np.max(np.abs(to_f64(lse) - rl)) < 1e-5, order
+
+
+# ----------------------------------------------------------------------------- staging copy
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout,cp", [("contiguous", 4), ("zigzag", 3)])
+def test_stage_kv_bit_exact(ctx, dtype, layout, cp):
+    """ra_stage_kv copies owner o's K and V chunk (rows [o S/cp, (o+1) S/cp) of the ring
+    tensors) into the destination, K then V, bit for bit."""
+    B, Hq, Hkv, D = 2, 4, 2, 64
+    S = 2 * cp * 36
+    prob = api.Problem(B, S, Hq, Hkv, D, cp, layout, dtype)
+    k = to_dev(rand_store((B, Hkv, S, D), dtype, 141), dtype)
+    v = to_dev(rand_store((B, Hkv, S, D), dtype, 142), dtype)
+    k_ring = api.ra_layout_gather(ctx, prob, 0, cp, k)
+    v_ring = api.ra_layout_gather(ctx, prob, 0, cp, v)
+    c = prob.chunk
+    for owner in range(cp):
+        dst = api.ra_stage_kv(ctx, prob, owner, k_ring, v_ring)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(dst[0]), bits(k_ring[:, :, owner * c:(owner + 1) * c]))
+        assert np.array_equal(bits(dst[1]), bits(v_ring[:, :, owner * c:(owner + 1) * c]))
+    with pytest.raises(ValueError):
+        api.ra_stage_kv(ctx, prob, cp, k_ring, v_ring)
+
+
+def test_reshard_rejects_overlapping_buffers(ctx):
+    """Validation rejects src / dst ranges that overlap anywhere (not only equal pointers);
+    nothing is enqueued."""
+    prob = api.Problem(1, 256, 8, 8, 64, 4, "contiguous", "bf16")
+    n = 1 * 8 * 64 * 64  # batch * heads * S/cp * head_dim
+    buf = torch.zeros(2 * n + 64, dtype=torch.bfloat16, device="cuda")
+    src = buf[:n]
+    for off in (8, n - 8):
+        with pytest.raises(ValueError):
+            L.call("ra_ulysses_reshard", ctx.handle, __import__("ctypes").byref(prob.c()), 0, 8,
+                   api._ptr(src), api._ptr(buf[off:off + n]), None)
+    L.call("ra_ulysses_reshard", ctx.handle, __import__("ctypes").byref(prob.c()), 0, 8,
+           api._ptr(src), api._ptr(buf[n:2 * n]), None)
+    torch.cuda.synchronize()

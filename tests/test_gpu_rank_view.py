@@ -69,6 +69,10 @@ CASES = [
     (1, 64, 2, 1, 64, 3, "zigzag", "bf16"),
     (1, 64, 2, 2, 64, 8, "contiguous", "bf16"),
     (1, 64, 4, 1, 128, 8, "zigzag", "bf16"),
+    # cp 16, the long-ring degree: 15 staged steps, both slots and both dS buffers reused many
+    # times, the second running state and second dK/dV stream
+    (1, 64, 4, 2, 128, 16, "zigzag", "bf16"),
+    (1, 64, 4, 2, 128, 16, "contiguous", "bf16"),
 ]
 
 
@@ -154,6 +158,10 @@ SPLIT_CASES = [
     (1, 64, 2, 1, 64, 3, "zigzag", "bf16"),
     (1, 64, 2, 2, 64, 8, "contiguous", "bf16"),
     (1, 64, 4, 1, 128, 8, "zigzag", "bf16"),
+    # cp 16, the long-ring degree: 15 staged steps, both slots and both dS buffers reused many
+    # times, the second running state and second dK/dV stream
+    (1, 64, 4, 2, 128, 16, "zigzag", "bf16"),
+    (1, 64, 4, 2, 128, 16, "contiguous", "bf16"),
 ]
 
 
@@ -269,9 +277,21 @@ def test_large_scores_and_wide_gqa(ctx, dtype):
         assert np.max(np.abs(to_f64(lse) - rl)) < (1e-4 if dtype == "f32" else 2e-2)
         pos = O.rank_positions(S, cp, layout, rank)
         rdq, rdk, rdv = O.rank_view_bwd(q64, k64, v64, do64[:, :, pos], cp, layout, rank, 1.0)
-        # gradients carry the scale (1 here, ~11x the default): compare relative to their size
+        # bf16: per-tensor relative L2 (the dS operand is rounded to bf16, relative 2^-9 per
+        # element, and dQ = sum_j dS_j k_j cancels, sum_j dS_j = 0, so at scores sqrt(D) larger
+        # than the default an elementwise bound tied to |ref| does not hold).  fp32: the 1e-5
+        # bound holds at the default scale; a score's rounding error grows with its size (sqrt(D)
+        # larger at scale 1) and dQ, dK carry the scale once more, so 1e-5 * D elementwise.
         for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk[:, :, order], "dK"), (dv, rdv[:, :, order], "dV")):
             g, r = to_f64(got), ref
-            rel = np.linalg.norm(g - r) / np.linalg.norm(r)
-            assert rel < (1e-5 if dtype == "f32" else 1e-2), (name, rank, rel)
             assert np.all(np.isfinite(g))
+            if dtype == "bf16":
+                rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+                print(f"{name} rank {rank}: relative L2 {rel:.3e}, max abs err {np.max(np.abs(g - r)):.3e}")
+                assert rel < 1e-2, (name, rank, rel)
+            else:
+                err = float(np.max(np.abs(g - r)))
+                print(f"{name} rank {rank}: max abs err {err:.3e} (max |ref| {np.max(np.abs(r)):.3e})")
+                assert err <= 1e-5 * D, (name, rank, err)
+                rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+                assert rel < 1e-5, (name, rank, rel)

@@ -19,7 +19,8 @@ from context_blockwise_causal_amd import api
 from context_blockwise_causal_amd.inputs import draw, f32_from_bf16_bits
 from context_blockwise_causal_amd.workloads import WORKLOADS
 from oracle import attn64 as O
-from tests.gpu_util import assert_close, to_dev, to_f64
+from tests.gpu_util import (assert_close, oracle_dq_rows, oracle_fwd_rows, stratified_rows, to_dev,
+                             to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,24 +97,27 @@ def test_large_workloads_sampled(ctx, name):
     k64 = {g: f64_sub(t, "k", [g]) for g in kv_heads}
     v64 = {g: f64_sub(t, "v", [g]) for g in kv_heads}
     order = O.ring_order(S, cp, wl.layout)
+    ring_index = np.empty(S, np.int64)
+    ring_index[order] = np.arange(S)
     rng = np.random.default_rng(wl.seed)
     for rank in wl.ranks:
         print(f"[{name}] rank {rank}", flush=True)
         out = run_rank(ctx, prob, dev, k_ring, v_ring, rank, wl.backward)
         pos = O.rank_positions(S, cp, wl.layout, rank)
         n = len(pos)
-        sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 62, replace=False)]))
+        # two rows of every 128-row query tile (the tile of the forward and dQ kernels)
+        sample = stratified_rows(n, 128, 2, rng)
         got = {k: to_f64(v) for k, v in out.items() if k in ("o", "lse", "dq")}
         for h in heads:
             g = h // n_rep
             rows = pos[sample]
             q = f64_sub(t, "q", [h], rows)
             do = f64_sub(t, "do", [h], rows)
-            ro, rl = O.attention_rows(q, k64[g], v64[g], rows, kpos)
+            ro, rl = oracle_fwd_rows(q, k64[g], v64[g], rows, kpos, block=32)
             assert_close(got["o"][:, h][:, sample], ro[:, 0], wl.dtype, f"O rank {rank} head {h}")
             assert np.max(np.abs(got["lse"][:, h][:, sample] - rl[:, 0])) < 2e-3
             if wl.backward:
-                rdq, _, _ = O.attention_rows_bwd(q, k64[g], v64[g], do, rows, kpos)
+                rdq = oracle_dq_rows(q, k64[g], v64[g], do, rows, kpos, block=16)
                 assert_close(got["dq"][:, h][:, sample], rdq[:, 0], wl.dtype, f"dQ rank {rank} head {h}")
         if not wl.backward:
             continue
@@ -122,8 +126,6 @@ def test_large_workloads_sampled(ctx, name):
         # keys at the end of the rank's last chunk: only the rank's rows after them see them
         last_chunk_end = int(pos[-1]) + 1
         tail = np.arange(last_chunk_end - 256, last_chunk_end)
-        ring_index = np.empty(S, np.int64)
-        ring_index[order] = np.arange(S)
         for g in kv_heads:
             grp = list(range(g * n_rep, (g + 1) * n_rep))
             q = f64_sub(t, "q", grp, tail)
@@ -150,3 +152,40 @@ def test_large_workloads_sampled(ctx, name):
                 assert torch.count_nonzero(dv[:, :, zero_from:]) == 0
         del out, dk, dv
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,rank", [("llama-gqa-cp8-zigzag", 0), ("llama-gqa-cp8-zigzag", 7),
+                                       ("long-ring-cp16-zigzag", 0)])
+def test_staged_owner_grads_every_element(ctx, name, rank):
+    """dK and dV of staged (FULL-pair) owners at full size, element by element: the owners of
+    ring steps 1 and 2, whose chunks were staged into slot 0 and slot 1 and whose dK/dV kernels
+    ran on the compute stream and on the second stream, with the per-owner zeroing and cast.
+    For each owner 64 keys at the start and 64 at the end of its chunk are compared for one
+    key/value group; the oracle takes every rank row that sees them (O and LSE over each row's
+    whole causal key prefix), then the keys' gradients from those rows (key_grads)."""
+    wl, prob, t, dev, k_ring, v_ring = setup(ctx, name)
+    S, cp, n_rep = wl.seq_len, wl.cp, wl.heads_q // wl.heads_kv
+    out = run_rank(ctx, prob, dev, k_ring, v_ring, rank, True)
+    dk, dv = to_f64(out["dk"][:, :1]), to_f64(out["dv"][:, :1])   # kv group 0, ring order
+    del out
+    torch.cuda.empty_cache()
+    g, grp = 0, list(range(n_rep))
+    pos = O.rank_positions(S, cp, wl.layout, rank)
+    kpos = np.arange(S)
+    k64, v64 = f64_sub(t, "k", [g]), f64_sub(t, "v", [g])
+    chunk = prob.chunk
+    for step in (1, 2):
+        owner, pairs = api.ra_plan_step(prob, rank, step)
+        assert any(p_[4] == 0 for p_ in pairs), "step must have a FULL pair"
+        opos = O.rank_positions(S, cp, wl.layout, owner)
+        sel_idx = np.concatenate([np.arange(64), np.arange(chunk - 64, chunk)])
+        sel = opos[sel_idx]                                    # sequence positions of the keys
+        rows = pos[pos >= sel.min()]                           # the rank rows that can see them
+        print(f"[{name}] rank {rank} step {step} owner {owner}: {len(rows)} rows", flush=True)
+        q = f64_sub(t, "q", grp, rows)
+        do = f64_sub(t, "do", grp, rows)
+        o, lse = oracle_fwd_rows(q, k64, v64, rows, kpos, block=64)
+        rdk, rdv = O.key_grads(q, k64[:, :, sel], v64[:, :, sel], do, rows, sel, o, lse)
+        ring_rows = owner * chunk + sel_idx
+        assert_close(dk[:, :, ring_rows], rdk, wl.dtype, f"dK owner {owner}")
+        assert_close(dv[:, :, ring_rows], rdv, wl.dtype, f"dV owner {owner}")

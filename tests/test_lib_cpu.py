@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES) | set(L.OTHER)
@@ -52,7 +52,17 @@ def test_workspace_sizes():
     state = rows * 64 * 4 + 2 * rows * 4
     assert api.ra_workspace_size(p, 0) == 2 * state + 2 * slot  # two states with two slots
     kvel = 2 * 4 * 4096 * 64
-    assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot
+    # bf16 backward: two stored-dS buffers of one step's pair (B * Hq * 1024 keys * 1024 queries)
+    ds = 2 * 12 * 1024 * 1024 * 2
+    assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot + 2 * ds
+    # the scratch of one step, through the chunk-level query: rows of keys padded to 128
+    assert api.ra_chunk_bwd_ds_size(p, 1024, 1024, [(0, 0, 1024, 1024, 0)]) == ds
+    assert api.ra_chunk_bwd_ds_size(p, 300, 200, [(0, 0, 150, 100, 0), (150, 0, 150, 100, 2)]) == \
+        2 * 12 * 150 * 128 * 2
+    assert api.ra_chunk_bwd_ds_size(p, 300, 300, [(0, 0, 150, 150, 1), (150, 0, 150, 150, 0)]) == \
+        2 * (2 * 12 * 150 * 256 * 2)
+    f32 = api.Problem(2, 4096, 12, 4, 64, 4, "contiguous", "f32")
+    assert api.ra_chunk_bwd_ds_size(f32, 1024, 1024, [(0, 0, 1024, 1024, 0)]) == 0
     assert api.ra_workspace_size(p, 2) == (1 + 4) * (rows * 64 * 4 + 2 * rows * 4)  # running + 4 partials
     two = api.Problem(2, 4096, 12, 4, 64, 2, "contiguous", "bf16")  # one staging slot, one state
     rows2 = 2 * 12 * 2048
@@ -126,3 +136,15 @@ def test_plan_positions_and_window_skips(layout, cp, window, chunk):
                 else:
                     assert vis.any()
                     assert KIND[causal] == mask  # the causal kind is kept; the kernel applies the rest
+
+
+def test_grid_row_limit_is_validated():
+    """The row-wise kernels put one (batch, head) per grid row (at most 65535): larger problems
+    are rejected by validation, before anything could be enqueued."""
+    big = api.Problem(65536, 256, 1, 1, 64, 1, "contiguous", "bf16")
+    with pytest.raises(ValueError) as e:
+        api.ra_validate(big)
+    assert e.value.status == L.RA_ERR_UNSUPPORTED
+    api.ra_validate(api.Problem(65535, 256, 1, 1, 64, 1, "contiguous", "bf16"))
+    with pytest.raises(ValueError):
+        api.ra_workspace_size(api.Problem(8192, 256, 16, 16, 64, 1, "contiguous", "bf16"), 0)
