@@ -90,7 +90,7 @@ __device__ __forceinline__ float row_bcast(float x, int r) {
   return __builtin_bit_cast(float, o);
 }
 
-template <int D>
+template <int D, bool DS>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   using C = KvCfg<D>;
   // The V tile and two buffers of (Q, dO), carved out of one LDS array (lse and delta travel in
@@ -166,16 +166,18 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const float* dltp = p.delta + qhead + pr.q_row0;
     // Stored scale * dS (bf16, query-major: q_len rows of ds_ld keys) of this (batch, query head)
     // and pair, at this workgroup's first key.
-    u16* const dsp = p.ds ? reinterpret_cast<u16*>(p.ds) + pr.ds_off +
-                                ((int64_t)tr.b * p.Hq + tr.hq) * pr.q_len * pr.ds_ld + kloc0
-                          : nullptr;
+    u16* const dsp = DS ? reinterpret_cast<u16*>(p.ds) + pr.ds_off +
+                              ((int64_t)tr.b * p.Hq + tr.hq) * pr.q_len * pr.ds_ld + kloc0
+                        : nullptr;
     // One query step on (Qs, dOs, ex); the next step's rows go into (nQ, ndO, nex).
     // (la, ld): raw lse / delta of this step's rows, loaded one step ahead.
     float la, ld;
-    // Stores the dS block staged by the step at query qb: thread t moves 16-byte chunks t and
-    // t + 256 (row = chunk / 16, 16 chunks per row), rows past the pair skipped.  Waves that were
-    // inactive in that step left stale values in their keys' columns; those (query, key) entries
-    // are excluded by the mask, and the dQ pass masks them out again.
+    // Stores the dS block staged by the step at query qb, right after that step's closing
+    // barrier: thread t moves 16-byte chunks t and t + 256 (row = chunk / 16, 16 chunks per row),
+    // rows past the pair skipped.  The stores are waited for at the end of the next step, which
+    // writes the other staging block.  Waves that were inactive in that step left stale values in
+    // their keys' columns; those (query, key) entries are excluded by the mask, and the dQ pass
+    // masks them out again.
     auto flush_ds = [&](const u16* __restrict__ blk, int64_t qb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -186,12 +188,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
       }
     };
     auto step = [&](const u16* __restrict__ Vs, const u16* __restrict__ Qs, const u16* __restrict__ dOs,
-                    u16* __restrict__ nQ, u16* __restrict__ ndO, u16* __restrict__ sw,
-                    const u16* __restrict__ sr, int it) {
+                    u16* __restrict__ nQ, u16* __restrict__ ndO, u16* __restrict__ sw, int it) {
       const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
-      // the previous step's dS block goes out before this step's loads, so that the loads' wait at
-      // the end of the step finds the stores long done
-      if (dsp && it > 0) flush_ds(sr, qbase - kKvBQ);
       // this lane's broadcast values: lse in base 2 (+inf past the pair, so that P vanishes) and
       // delta (0 past the pair)
       const bool rv = qbase + perm_reg_row(lane & 15, hh) < pr.q_len;
@@ -259,7 +257,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         // scale * dS (bf16, exactly the operand of dK) into the staged block for the dQ pass:
         // register 8c + e of this lane is query 16 c + 8 hh + e of the step, at its key's column
         // (extracted through 32-bit words)
-        if (dsp) {
+        if (DS) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const u32x4 wv = __builtin_bit_cast(u32x4, dsb[c]);
@@ -271,6 +269,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
       }
       wait_vmem();
       __syncthreads();
+      if (DS) flush_ds(sw, qbase);
     };
 
     issue_tile<D, kKvBQ, 4>(Qp + q_begin * D, pr.q_len - q_begin, qdbuf);
@@ -281,11 +280,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     for (int it = 0; it < niter; ++it) {
       u16* cur = qdbuf + (it & 1) * 2 * C::QT;
       u16* nxt = qdbuf + ((it + 1) & 1) * 2 * C::QT;
-      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, stage + (it & 1) * kDsStage,
-           stage + ((it + 1) & 1) * kDsStage, it);
+      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, stage + (it & 1) * kDsStage, it);
     }
-    // the last step's block (its writes are complete: the step ended with a barrier)
-    if (dsp) flush_ds(stage + ((niter - 1) & 1) * kDsStage, q_begin + (int64_t)(niter - 1) * kKvBQ);
   }
 
   // The query heads of one key/value head add into the same dK/dV rows, so the sums go out as
@@ -641,7 +637,7 @@ int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFo
   const int64_t nkv = kv.dk ? (int64_t)kv.B * kv.Hq * kv.tiles_per_head : 0;
   const int64_t nq = q.U ? (int64_t)q.B * q.Hq * q.tiles_per_head : 0;
   if (nkv > 0) {
-    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
+    hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, true>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   if (nq == 0) return 0;
@@ -676,7 +672,7 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
     qs = (hipStream_t)fork->side;
   }
   if (do_kv) {
-    hipLaunchKernelGGL(chunk_bwd_kv_kernel<D>, dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
+    hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, false>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   if (do_q) {
