@@ -36,15 +36,6 @@ constexpr int kNT = 256;
 
 constexpr int kKvBN = 128;  // keys per workgroup
 constexpr int kKvBQ = 32;   // query rows per step
-constexpr int kDsStage = kKvBQ * kKvBN;  // elements of one staged dS block (32 queries x 128 keys)
-
-// Staged dS block: row q (query of the step) holds the 128 keys of the workgroup in 16-byte
-// chunks; chunk c of row q sits at chunk position c ^ (4 ((q >> 3) & 1)), which keeps the 2-byte
-// writes of a step (one row per lane half, rows 8 apart) and the 16-byte row reads of the
-// store on distinct banks.
-__device__ __forceinline__ int stage_off(int q, int key) {
-  return q * kKvBN + ((((key >> 3) ^ (((q >> 3) & 1) << 2))) << 3) + (key & 7);
-}
 
 template <int D>
 struct KvCfg {
@@ -99,14 +90,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   // __restrict__ parameter, which lets the compiler prove that those loads do not alias its reads
   // (so it does not wait for them before the step's LDS reads).  One array, not several: with
   // several LDS variables the compiler's LDS lowering replaces the pointer-based alias scopes.
-  // Two more blocks of 32 queries x 128 keys stage the workgroup's scale * dS for the dQ pass:
-  // each step's wavefronts write their 32 x 32 blocks there, and the next step stores the whole
-  // block query-major (256 contiguous bytes per query row), which takes a quarter of the cache
-  // lines per store instruction that per-lane key rows would.
-  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT + 2 * kDsStage];
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT];
   u16* const vt = lds;
   u16* const qdbuf = lds + kKvBN * D;
-  u16* const stage = qdbuf + 4 * C::QT;
 
   const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -164,31 +150,16 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
     const float* lsep = p.lse + qhead + pr.q_row0;
     const float* dltp = p.delta + qhead + pr.q_row0;
-    // Stored scale * dS (bf16, query-major: q_len rows of ds_ld keys) of this (batch, query head)
-    // and pair, at this workgroup's first key.
+    // Stored scale * dS^T (bf16, key-major: ds_rows keys of ds_ld queries) of this (batch, query
+    // head) and pair, at this lane's key row.
     u16* const dsp = DS ? reinterpret_cast<u16*>(p.ds) + pr.ds_off +
-                              ((int64_t)tr.b * p.Hq + tr.hq) * pr.q_len * pr.ds_ld + kloc0
+                              (((int64_t)tr.b * p.Hq + tr.hq) * pr.ds_rows + kloc0 + kl) * pr.ds_ld
                         : nullptr;
-    // One query step on (Qs, dOs, ex); the next step's rows go into (nQ, ndO, nex).
+    // One query step on (Qs, dOs); the next step's rows go into (nQ, ndO).
     // (la, ld): raw lse / delta of this step's rows, loaded one step ahead.
     float la, ld;
-    // Stores the dS block staged by the step at query qb, right after that step's closing
-    // barrier: thread t moves 16-byte chunks t and t + 256 (row = chunk / 16, 16 chunks per row),
-    // rows past the pair skipped.  The stores are waited for at the end of the next step, which
-    // writes the other staging block.  Waves that were inactive in that step left stale values in
-    // their keys' columns; those (query, key) entries are excluded by the mask, and the dQ pass
-    // masks them out again.
-    auto flush_ds = [&](const u16* __restrict__ blk, int64_t qb) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = tid + 256 * h, row = idx >> 4, ch = idx & 15;
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(blk + row * kKvBN + ((ch ^ (((row >> 3) & 1) << 2)) << 3));
-        if (qb + row < pr.q_len)
-          __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(dsp + (qb + row) * pr.ds_ld + ch * 8));
-      }
-    };
     auto step = [&](const u16* __restrict__ Vs, const u16* __restrict__ Qs, const u16* __restrict__ dOs,
-                    u16* __restrict__ nQ, u16* __restrict__ ndO, u16* __restrict__ sw, int it) {
+                    u16* __restrict__ nQ, u16* __restrict__ ndO, int it) {
       const int64_t qbase = q_begin + (int64_t)it * kKvBQ;
       // this lane's broadcast values: lse in base 2 (+inf past the pair, so that P vanishes) and
       // delta (0 past the pair)
@@ -199,7 +170,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         issue_tile<D, kKvBQ, 4>(dOp + (qbase + kKvBQ) * D, pr.q_len - qbase - kKvBQ, ndO);
         kv_load_rows(lsep, dltp, qbase + kKvBQ, pr.q_len, la, ld);
       }
-      // The whole wavefront lies in the future of every query of this step (diagonal pairs).
+      // The whole wavefront lies in the future of every query of this step (diagonal pairs).  A
+      // wavefront that the step does not reach stores no dS: its entries are excluded, and the
+      // dQ pass masks them.
       const bool active = !(diag && kloc0 + 32 * w > qbase + kKvBQ - 1) && !(has_hi && qbase > wave_hi_max);
       if (active) {
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -246,6 +219,19 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
           pb[c] = a;
           dsb[c] = b;
         }
+        // scale * dS (bf16, exactly the operand of dK) for the dQ pass: registers 8c .. 8c+7 of
+        // this lane are queries 16 c + 8 hh .. +7 of the step at its key, i.e. 16 contiguous bytes
+        // of the key's dS^T row.  Key rows past the range (the block has 128-row granules) and
+        // query columns past the pair (up to ds_ld) get values that nothing reads.  The two halves
+        // of a 64-byte row segment come from the two lane halves of one instruction, and the next
+        // step fills the rest of the cache line.  The stores go out ahead of the dV / dK
+        // contractions, which give them time to complete before the wait that ends the step.
+        if (DS) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            *reinterpret_cast<bf16x8*>(dsp + qbase + 16 * c + 8 * hh) = dsb[c];
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the tiles.
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
@@ -254,22 +240,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
             dv_acc[db] = mfma32(tr_operand(dOs, ta, D, c, db), pb[c], dv_acc[db]);
             dk_acc[db] = mfma32(tr_operand(Qs, ta, D, c, db), dsb[c], dk_acc[db]);
           }
-        // scale * dS (bf16, exactly the operand of dK) into the staged block for the dQ pass:
-        // register 8c + e of this lane is query 16 c + 8 hh + e of the step, at its key's column
-        // (extracted through 32-bit words)
-        if (DS) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const u32x4 wv = __builtin_bit_cast(u32x4, dsb[c]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              sw[stage_off(16 * c + 8 * hh + e, kl)] = (u16)(wv[e >> 1] >> (16 * (e & 1)));
-          }
-        }
       }
       wait_vmem();
       __syncthreads();
-      if (DS) flush_ds(sw, qbase);
     };
 
     issue_tile<D, kKvBQ, 4>(Qp + q_begin * D, pr.q_len - q_begin, qdbuf);
@@ -280,7 +253,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     for (int it = 0; it < niter; ++it) {
       u16* cur = qdbuf + (it & 1) * 2 * C::QT;
       u16* nxt = qdbuf + ((it + 1) & 1) * 2 * C::QT;
-      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, stage + (it & 1) * kDsStage, it);
+      step(vt, cur, cur + C::QT, nxt, nxt + C::QT, it);
     }
   }
 
@@ -494,28 +467,28 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 
 // ======================================================================= dQ from stored dS
 //
-// The dK/dV kernel writes scale * dS (bf16, the operand it feeds to dK) query-major, one row of
-// keys per query.  dQ is then the plain contraction dQ += (scale dS) K: one workgroup = 4
+// The dK/dV kernel writes scale * dS^T (bf16, the operand it feeds to dK) key-major, one row of
+// queries per key.  dQ is then the plain contraction dQ += (scale dS) K: one workgroup = 4
 // wavefronts = 128 query rows of one (batch, head), a lane one query; per tile of 64 keys the K
-// tile and the workgroup's 128 x 64 block of dS are staged in LDS (direct loads, one tile ahead)
-// and dQ^T += K^T dS^T, K^T read transposed and dS^T as row reads (a lane's query row holds its
-// keys contiguously).  The kernel is bound by reading dS from HBM (two bytes per (query, key) pair
-// against 2 D FLOPs).
+// tile and the workgroup's 64 x 128 block of dS^T are staged in LDS (direct loads, one tile
+// ahead) and dQ^T += K^T dS^T, with both operands read transposed out of their [key][..] tiles
+// (ds_read_b64_tr_b16).  The kernel is bound by reading dS from HBM (two bytes per (query, key)
+// pair against 2 D FLOPs).
 //
-// Entries of dS that no query of a pair sees may never have been written, or hold stale values
+// Entries of dS^T that no query of a pair sees may never have been written, or hold stale values
 // (the dK/dV kernel skips query steps that lie wholly before its keys or past their window, and
-// wavefronts whose keys a step does not reach leave their columns of the staged block as they
-// were), so tiles that straddle a mask bound zero the excluded entries of the operand before the
-// MFMA; interior tiles are fully visible and were written.
+// wavefronts whose keys a step does not reach store nothing), so tiles that straddle a mask bound
+// zero the excluded entries of the operand before the MFMA; interior tiles are fully visible and
+// were written.
 
-constexpr int kDsBM = 128;  // query rows per workgroup (= columns of a stored dS^T row block)
-constexpr int kDsBN = 64;   // keys per tile
+constexpr int kDsBM = 128;  // query rows per workgroup (columns of a dS^T tile)
+constexpr int kDsBN = 64;   // keys per tile (rows of a dS^T tile)
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p) {
   constexpr int DB = D / 32;
   constexpr int KT = kDsBN * D;       // elements of one K tile
-  constexpr int ST = kDsBM * kDsBN;   // elements of one dS tile (128 queries x 64 keys)
+  constexpr int ST = kDsBN * kDsBM;   // elements of one dS^T tile (64 keys x 128 queries)
   // two buffers of (K tile, dS^T tile), read and filled through __restrict__ pointers
   __shared__ __attribute__((aligned(16))) u16 buf[2 * (KT + ST)];
 
@@ -531,8 +504,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
-  const TrAddr kt = make_tr_addr(lane, D);          // K^T out of the [key][d] tile
-  const RowAddr sa = make_row_addr(qi, hh, kDsBN);  // this lane's query row of the dS tile
+  const TrAddr kt = make_tr_addr(lane, D);      // K^T out of the [key][d] tile
+  const TrAddr st = make_tr_addr(lane, kDsBM);  // dS^T columns out of the [key][query] tile
   const u16* Kg = reinterpret_cast<const u16*>(p.k);
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
@@ -544,9 +517,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
     if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
     const int nkt = (int)((key_end + kDsBN - 1) / kDsBN);
     const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
-    // this workgroup's 128 query rows of the pair's dS block (rows of ds_ld keys)
-    const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + (head * pr.q_len + qloc0) * pr.ds_ld;
-    const int64_t q_left = pr.q_len - qloc0;  // valid query rows of the tile
+    // this workgroup's 128 query columns of the pair's dS^T block (rows of ds_ld queries)
+    const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + head * pr.ds_rows * pr.ds_ld + qloc0;
     const int64_t wq_first = qloc0 + 32 * w;
     const bool wave_has_rows = 32 * w < tr.nrows;
     const bool has_lo = p.window > 0 || p.attn_chunk > 0;
@@ -564,15 +536,16 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
       const int64_t kbase = (int64_t)t * kDsBN;
       if (t + 1 < nkt) {
         issue_tile<D, kDsBN, 4>(Kp + (kbase + kDsBN) * D, pr.kv_len - kbase - kDsBN, nk);
-        issue_tile_pitched<kDsBN, kDsBM, 4>(Sp + kbase + kDsBN, pr.ds_ld, q_left, ns);
+        issue_tile_pitched<kDsBM, kDsBN, 4>(Sp + (kbase + kDsBN) * pr.ds_ld, pr.ds_ld,
+                                            pr.kv_len - kbase - kDsBN, ns);
       }
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
                           !(has_lo && kbase + kDsBN - 1 < wave_lo);
       if (active) {
-        // B operand dS^T for key step c: lane holds dS[its query][16c + 8hh + e], e = 0..7
+        // B operand dS^T for key step c: lane holds dS^T[16c + 8hh + e][its query], e = 0..7
         bf16x8 dsb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dsb[c] = row_operand(sb, sa, c);
+        for (int c = 0; c < 4; ++c) dsb[c] = tr_operand(sb, st, kDsBM, c, w);
         const bool edge = (kbase + kDsBN > pr.kv_len) || (diag && kbase + kDsBN - 1 > wq_first) ||
                           (has_lo && kbase < wave_lo_max);
         if (edge) {
@@ -607,7 +580,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
 
     if (kt0 >= nkt) continue;  // uniform over the workgroup
     issue_tile<D, kDsBN, 4>(Kp + kt0 * kDsBN * D, pr.kv_len - kt0 * kDsBN, buf);
-    issue_tile_pitched<kDsBN, kDsBM, 4>(Sp + kt0 * kDsBN, pr.ds_ld, q_left, buf + KT);
+    issue_tile_pitched<kDsBM, kDsBN, 4>(Sp + kt0 * kDsBN * pr.ds_ld, pr.ds_ld, pr.kv_len - kt0 * kDsBN,
+                                        buf + KT);
     wait_vmem();
     __syncthreads();
     for (int t = (int)kt0; t < nkt; ++t) {

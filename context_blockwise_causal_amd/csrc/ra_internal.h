@@ -70,10 +70,10 @@ struct KPair {
   int64_t q_row0, kv_row0, q_len, kv_len;
   int32_t mask, pad_;
   int64_t q_pos0, kv_pos0;  // sequence positions of the first query / key row
-  // Backward with stored dS: the pair's dS block starts ds_off elements into KParams::ds; it
-  // holds, per (batch, query head), q_len rows (queries) of ds_ld elements (keys, ds_ld a
-  // multiple of 128 >= kv_len).
-  int64_t ds_off, ds_ld;
+  // Backward with stored dS: the pair's dS^T block starts ds_off elements into KParams::ds; it
+  // holds, per (batch, query head), ds_rows rows (keys; kv_len rounded up to 128) of ds_ld
+  // elements (queries; q_len rounded up to 128).
+  int64_t ds_off, ds_rows, ds_ld;
 };
 
 struct KParams {
@@ -108,8 +108,10 @@ struct KParams {
 // `tile_rows` rows.  by_q selects the forward grouping (Q ranges) or the backward (K/V).
 void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64_t tile_rows);
 // Lays out the stored-dS scratch of a pair list (bytes; 0 when no pair computes) and, when kp is
-// given, fills the pairs' ds_off / ds_ld (call after build_ranges).  Each non-SKIP pair gets
-// B * Hq * q_len * ds_ld bf16 values, ds_ld = kv_len rounded up to 128, blocks 256-byte aligned.
+// given, fills the pairs' ds_off / ds_rows / ds_ld (call after build_ranges).  Each non-SKIP pair
+// gets B * Hq * ds_rows * ds_ld bf16 values (dS^T, key-major), ds_rows = kv_len rounded up to
+// 128 (the dK/dV workgroup's key granule) and ds_ld = q_len rounded up to 128, blocks 256-byte
+// aligned.
 size_t ds_layout(const Shape& s, const ra_pair* pairs, int32_t n, KParams* kp);
 // Largest ds_layout over the ring steps of a rank view (the size of one dS buffer).
 size_t ds_step_max(const Shape& s, int32_t rank);

@@ -214,12 +214,13 @@ size_t ds_layout(const Shape& s, const ra_pair* pairs, int32_t n, KParams* kp) {
   for (int i = 0; i < n; ++i) {
     const ra_pair& p = pairs[i];
     if (p.mask == RA_MASK_SKIP || p.q_len == 0 || p.kv_len == 0) continue;
-    const int64_t ld = (p.kv_len + 127) / 128 * 128;
+    const int64_t rows = (p.kv_len + 127) / 128 * 128, ld = (p.q_len + 127) / 128 * 128;
     if (kp) {
       kp->pairs[i].ds_off = (int64_t)off;
+      kp->pairs[i].ds_rows = rows;
       kp->pairs[i].ds_ld = ld;
     }
-    off += align256((size_t)(s.B * s.Hq * p.q_len * ld) * 2) / 2;
+    off += align256((size_t)(s.B * s.Hq * rows * ld) * 2) / 2;
   }
   return off * 2;
 }

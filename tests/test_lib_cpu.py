@@ -55,12 +55,13 @@ def test_workspace_sizes():
     # bf16 backward: two stored-dS buffers of one step's pair (B * Hq * 1024 keys * 1024 queries)
     ds = 2 * 12 * 1024 * 1024 * 2
     assert api.ra_workspace_size(p, 1) == rows * 64 * 4 + 2 * kvel * 4 + rows * 4 + 2 * slot + 2 * ds
-    # the scratch of one step, through the chunk-level query: rows of keys padded to 128
+    # the scratch of one step, through the chunk-level query: dS^T blocks of key rows x query
+    # columns, both padded to 128; SKIP pairs take none
     assert api.ra_chunk_bwd_ds_size(p, 1024, 1024, [(0, 0, 1024, 1024, 0)]) == ds
     assert api.ra_chunk_bwd_ds_size(p, 300, 200, [(0, 0, 150, 100, 0), (150, 0, 150, 100, 2)]) == \
-        2 * 12 * 150 * 128 * 2
+        2 * 12 * 128 * 256 * 2
     assert api.ra_chunk_bwd_ds_size(p, 300, 300, [(0, 0, 150, 150, 1), (150, 0, 150, 150, 0)]) == \
-        2 * (2 * 12 * 150 * 256 * 2)
+        2 * (2 * 12 * 256 * 256 * 2)
     f32 = api.Problem(2, 4096, 12, 4, 64, 4, "contiguous", "f32")
     assert api.ra_chunk_bwd_ds_size(f32, 1024, 1024, [(0, 0, 1024, 1024, 0)]) == 0
     assert api.ra_workspace_size(p, 2) == (1 + 4) * (rows * 64 * 4 + 2 * rows * 4)  # running + 4 partials
