@@ -233,15 +233,16 @@ def stored_traffic(wl_name, kernel):
 
 def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes, stage_bytes):
     """Turns two rocprofv3 --pmc runs of `--kernels-only` (FETCH_SIZE, then WRITE_SIZE; KiB per
-    dispatch) into bytes per launch, scaled by what the counters read for a calibration copy:
-    the layout kernel gathering one K tensor (calib_bytes read and written).  The staging copy
-    (copy2d_kernel, stage_bytes read and written per dispatch, a different kernel and size)
-    gives a second, independent factor; the record keeps both."""
+    dispatch) into bytes per launch, scaled by what the counters read for a calibration copy of
+    known size: the last layout-kernel dispatch of the run, which gathers one K tensor (calib_bytes
+    read and written).  (The run's earlier layout dispatches gather tensors of other sizes.)  The
+    staging copies (copy2d_kernel, stage_bytes read and written per dispatch, a different kernel and
+    size) give a second, independent factor; the record keeps both."""
     import csv
     import glob
     import re
 
-    def per_kernel(root, counter):
+    def per_dispatch(root, counter):
         acc = {}
         for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
@@ -251,22 +252,29 @@ def traffic_summary(wl_name, fetch_dir, write_dir, calib_bytes, stage_bytes):
                 if not m:
                     continue
                 a = acc.setdefault(m.group(1), {})
-                a[r["Dispatch_Id"]] = a.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"]) * 1024
-        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+                d = int(r["Dispatch_Id"])
+                a[d] = a.get(d, 0.0) + float(r["Counter_Value"]) * 1024
+        return acc
 
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    fs, ws = calib_bytes / fetch["layout_kernel"], calib_bytes / write["layout_kernel"]
+    def avg(d):
+        return sum(d.values()) / len(d)
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    cal_f = fetch["layout_kernel"][max(fetch["layout_kernel"])]
+    cal_w = write["layout_kernel"][max(write["layout_kernel"])]
+    fs, ws = calib_bytes / cal_f, calib_bytes / cal_w
     rec = {"workload": wl_name, "source_hash": source_hash(),
-           "calibration": {"kernel": "layout_kernel", "bytes_each_way": calib_bytes,
-                           "fetch_read": fetch["layout_kernel"], "write_read": write["layout_kernel"],
+           "calibration": {"kernel": "layout_kernel (last dispatch: the gather of one K tensor)",
+                           "bytes_each_way": calib_bytes, "fetch_read": cal_f, "write_read": cal_w,
                            "fetch_scale": fs, "write_scale": ws},
-           "kernels": {k: {"fetch_bytes_per_launch": fetch[k] * fs, "write_bytes_per_launch": write[k] * ws}
+           "kernels": {k: {"fetch_bytes_per_launch": avg(fetch[k]) * fs, "write_bytes_per_launch": avg(write[k]) * ws,
+                           "launches": len(fetch[k])}
                        for k in fetch if k.startswith("chunk_") and k in write}}
     if "copy2d_kernel" in fetch and "copy2d_kernel" in write:
         rec["check"] = {"kernel": "copy2d_kernel", "bytes_each_way": stage_bytes,
-                        "fetch_read": fetch["copy2d_kernel"], "write_read": write["copy2d_kernel"],
-                        "fetch_scale": stage_bytes / fetch["copy2d_kernel"],
-                        "write_scale": stage_bytes / write["copy2d_kernel"]}
+                        "fetch_read": avg(fetch["copy2d_kernel"]), "write_read": avg(write["copy2d_kernel"]),
+                        "fetch_scale": stage_bytes / avg(fetch["copy2d_kernel"]),
+                        "write_scale": stage_bytes / avg(write["copy2d_kernel"])}
     with open(traffic_path(wl_name), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))

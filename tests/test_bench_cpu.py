@@ -46,11 +46,14 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
         return str(d)
     calib = 1 << 20
     stage = 1 << 16
-    fdir = write("f", "FETCH_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 2),
+    # an earlier layout dispatch gathers a tensor of another size; the calibration is the last one
+    fdir = write("f", "FETCH_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 8),
+                                     ("ra::layout_kernel(...)", calib / 1024 / 2),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 100.0),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 300.0),
                                      ("ra::copy2d_kernel(...)", stage / 1024 / 3)])
-    wdir = write("w", "WRITE_SIZE", [("ra::layout_kernel(...)", calib / 1024),
+    wdir = write("w", "WRITE_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 4),
+                                     ("ra::layout_kernel(...)", calib / 1024),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
                                      ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
                                      ("ra::copy2d_kernel(...)", stage / 1024 / 1.5)])
