@@ -16,6 +16,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
 RA_MASK_FULL, RA_MASK_DIAG, RA_MASK_SKIP = 0, 1, 2
 RA_A2A_SEQ_PACK, RA_A2A_HEAD_UNPACK, RA_A2A_HEAD_PACK, RA_A2A_SEQ_UNPACK = 0, 1, 2, 3
+RA_NOALLOC_SCRATCH_BYTES = 64 << 20  # size of the static scratch of ra_chunk_bwd_ds_noalloc
 
 
 class ra_problem(ctypes.Structure):
@@ -72,6 +73,8 @@ SIGNATURES = {
     "ra_chunk_bwd_ds_size": [_PROB, _I64, _I64, _PAIRS, _I32, ctypes.POINTER(ctypes.c_size_t)],
     "ra_chunk_bwd_ds": [_P, _PROB, _P, _P, _FP, _FP, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP,
                         _FP, _P, ctypes.c_size_t, _P],
+    "ra_chunk_bwd_ds_noalloc": [_P, _PROB, _P, _P, _FP, _FP, _I64, _P, _P, _I64, _PAIRS, _I32, _FP, _FP,
+                                _FP, _P],
     "ra_cast_from_f32": [_P, _PROB, _I64, _FP, _P, _P],
     "ra_rank_view_fwd": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],
     "ra_rank_view_fwd_split": [_P, _PROB, _I32, _P, _P, _P, _P, _FP, _P, ctypes.c_size_t, _P, _P],

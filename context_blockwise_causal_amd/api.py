@@ -339,6 +339,33 @@ def ra_chunk_bwd_ds(ctx, prob: Problem, q, dO, lse, delta, k, v, pairs, dq_acc, 
     return scratch
 
 
+def ra_chunk_bwd_ds_noalloc(ctx, prob: Problem, q, dO, lse, delta, k, v, pairs, dq_acc, dk_acc, dv_acc,
+                            stream=None):
+    """ra_chunk_bwd_ds with the library's static scratch (no device allocation by the call): at most
+    RA_NOALLOC_SCRATCH_BYTES of stored dS; calls that overlap on one GPU race for it."""
+    q_rows = q.shape[2]
+    kv_rows = k.shape[2]
+    qs = (prob.batch, prob.heads_q, q_rows)
+    ks = (prob.batch, prob.heads_kv, kv_rows, prob.head_dim)
+    _need(q, qs + (prob.head_dim,), prob.torch_dtype, "q")
+    _need(dO, qs + (prob.head_dim,), prob.torch_dtype, "dO")
+    _need(lse, qs, torch.float32, "lse")
+    _need(delta, qs, torch.float32, "delta")
+    _need(k, ks, prob.torch_dtype, "k")
+    _need(v, ks, prob.torch_dtype, "v")
+    if dq_acc is not None:
+        _need(dq_acc, qs + (prob.head_dim,), torch.float32, "dq_acc")
+    if dk_acc is not None:
+        _need(dk_acc, ks, torch.float32, "dk_acc")
+    if dv_acc is not None:
+        _need(dv_acc, ks, torch.float32, "dv_acc")
+    p = prob.c()
+    arr = L.pairs_array(pairs)
+    L.call("ra_chunk_bwd_ds_noalloc", ctx.handle, ctypes.byref(p), _ptr(q), _ptr(dO), _ptr(lse), _ptr(delta),
+           q_rows, _ptr(k), _ptr(v), kv_rows, arr, len(pairs), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
+           _stream(stream))
+
+
 def ra_cast_from_f32(ctx, prob: Problem, src, dst=None, stream=None):
     if src.dtype != torch.float32 or not src.is_contiguous():
         raise ValueError("src must be a contiguous float32 tensor")

@@ -32,6 +32,7 @@ struct ra_context {
   hipEvent_t qfreed[2];        // the backward ring's dQ kernels have finished reading a slot
   hipEvent_t ajoin;            // the ring's second compute stream has finished
   hipEvent_t dslocal;          // the backward's local-step dQ kernel has read its dS buffer
+  void* noalloc_scratch;       // this device's static scratch (ra_chunk_bwd_ds_noalloc)
 };
 
 namespace ra {
@@ -319,6 +320,11 @@ ra_status ra_create(int32_t device, ra_context** out) {
     release(c);  // the handles created before the failure
     return fail(RA_ERR_DEVICE, "event or stream creation failed: %s", hipGetErrorString(e));
   }
+  // the static scratch's address on this device (the device is current here)
+  if ((e = (hipError_t)noalloc_scratch_address(device, &c->noalloc_scratch)) != hipSuccess) {
+    release(c);
+    return fail(RA_ERR_DEVICE, "address of the static scratch on device %d: %s", device, hipGetErrorString(e));
+  }
   *out = c;
   return RA_OK;
 }
@@ -495,11 +501,16 @@ ra_status ra_chunk_bwd_ds_size(const ra_problem* prob, int64_t q_rows, int64_t k
   return RA_OK;
 }
 
-ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* prob, const void* q, const void* dO,
-                          const float* lse, const float* delta, int64_t q_rows, const void* k,
-                          const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
-                          float* dq_acc, float* dk_acc, float* dv_acc, void* scratch,
-                          size_t scratch_bytes, void* stream) {
+namespace ra {
+namespace {
+
+// ra_chunk_bwd_ds and ra_chunk_bwd_ds_noalloc: the same call with the scratch given (`fixed` =
+// false: a caller buffer, too small is RA_ERR_WORKSPACE) or the static one (`fixed` = true).
+ra_status chunk_bwd_ds(ra_context* ctx, const ra_problem* prob, const void* q, const void* dO,
+                       const float* lse, const float* delta, int64_t q_rows, const void* k,
+                       const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
+                       float* dq_acc, float* dk_acc, float* dv_acc, void* scratch,
+                       size_t scratch_bytes, void* stream, bool fixed) {
   Shape s;
   ra_status st = common(ctx, prob, &s);
   if (st != RA_OK) return st;
@@ -524,12 +535,41 @@ ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* prob, const void* q
     return dev_err(run_bwd(s, kp, pairs, n_pairs, stream, nullptr), "chunk backward");
   }
   const size_t need = ds_layout(s, pairs, n_pairs, nullptr);
-  if (need > 0 && (!scratch || !aligned16(scratch)))
-    return fail(RA_ERR_INVALID, "scratch is NULL or not 16-byte aligned");
-  if (scratch_bytes < need)
-    return fail(RA_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, need);
+  if (fixed) {
+    if (need > scratch_bytes)
+      return fail(RA_ERR_WORKSPACE, "the stored dS needs %zu bytes; the static scratch holds %zu", need,
+                  scratch_bytes);
+  } else {
+    if (need > 0 && (!scratch || !aligned16(scratch)))
+      return fail(RA_ERR_INVALID, "scratch is NULL or not 16-byte aligned");
+    if (scratch_bytes < need)
+      return fail(RA_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, need);
+  }
   DeviceGuard g(ctx->device);
   return dev_err(run_bwd_ds(s, kp, pairs, n_pairs, scratch, stream, nullptr), "chunk backward (stored dS)");
+}
+
+}  // namespace
+}  // namespace ra
+
+ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* prob, const void* q, const void* dO,
+                          const float* lse, const float* delta, int64_t q_rows, const void* k,
+                          const void* v, int64_t kv_rows, const ra_pair* pairs, int32_t n_pairs,
+                          float* dq_acc, float* dk_acc, float* dv_acc, void* scratch,
+                          size_t scratch_bytes, void* stream) {
+  return ra::chunk_bwd_ds(ctx, prob, q, dO, lse, delta, q_rows, k, v, kv_rows, pairs, n_pairs, dq_acc,
+                          dk_acc, dv_acc, scratch, scratch_bytes, stream, false);
+}
+
+ra_status ra_chunk_bwd_ds_noalloc(ra_context* ctx, const ra_problem* prob, const void* q,
+                                  const void* dO, const float* lse, const float* delta,
+                                  int64_t q_rows, const void* k, const void* v, int64_t kv_rows,
+                                  const ra_pair* pairs, int32_t n_pairs, float* dq_acc,
+                                  float* dk_acc, float* dv_acc, void* stream) {
+  clear_error();
+  if (!ctx) return ra::fail(RA_ERR_INVALID, "context is NULL");
+  return ra::chunk_bwd_ds(ctx, prob, q, dO, lse, delta, q_rows, k, v, kv_rows, pairs, n_pairs, dq_acc,
+                          dk_acc, dv_acc, ctx->noalloc_scratch, RA_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* prob, int64_t n, const float* src,

@@ -156,6 +156,10 @@ int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, con
 // (q.ds set, Q-major ranges): dq += dS K.  With `fork` the dQ kernel runs on `side` after the
 // dK/dV kernel (fork event recorded after it), joined into `stream` when fork->join is set.
 int launch_chunk_bwd_ds_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork);
+// Device address of this GPU's copy of the static scratch of ra_chunk_bwd_ds_noalloc (looked up
+// once per device; `device` must be current).  Returns a hipError_t.
+constexpr int kMaxDevices = 64;
+int noalloc_scratch_address(int device, void** out);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
 constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)

@@ -272,6 +272,22 @@ ra_status ra_chunk_bwd_ds(ra_context* ctx, const ra_problem* problem, const void
                           int32_t n_pairs, float* dq_acc, float* dk_acc, float* dv_acc,
                           void* scratch, size_t scratch_bytes, void* stream);
 
+/* The same call for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): ra_chunk_bwd_ds with the scratch taken
+ * from a static device array of RA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * GPU it runs on until the process ends (its address is looked up once per device, in ra_create).
+ * The call allocates nothing.  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's dS: calls that overlap on one GPU (on different streams, or from several threads or
+ * contexts) race, and a second-phase call (dk_acc = dv_acc = NULL) reads whatever the last
+ * first-phase call on that GPU wrote.  RA_ERR_WORKSPACE when ra_chunk_bwd_ds_size exceeds
+ * RA_NOALLOC_SCRATCH_BYTES; otherwise arguments, results and errors as for ra_chunk_bwd_ds. */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ra_status ra_chunk_bwd_ds_noalloc(ra_context* ctx, const ra_problem* problem, const void* q,
+                                  const void* dO, const float* lse, const float* delta,
+                                  int64_t q_rows, const void* k, const void* v, int64_t kv_rows,
+                                  const ra_pair* pairs, int32_t n_pairs, float* dq_acc,
+                                  float* dk_acc, float* dv_acc, void* stream);
+
 /* Casts n fp32 values to problem->dtype (round to nearest even for bf16): the backward's
  * final step for dQ / dK / dV accumulators. */
 ra_status ra_cast_from_f32(ra_context* ctx, const ra_problem* problem, int64_t n,
