@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
 
 SOURCES = ["ra_plan.cpp", "ra_host.cpp", "kern_rowops.hip", "kern_fwd.hip", "kern_bwd.hip",
-           "kern_f32.hip"]
+           "kern_f32.hip", "ra_scratch.hip"]
 
 ARCH = os.environ.get("RA_OFFLOAD_ARCH", "gfx950")
 

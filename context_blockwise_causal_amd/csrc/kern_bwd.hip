@@ -16,8 +16,6 @@
 // unpadded and chunk-swizzled (conflict-free row reads, ds_read_b64_tr_b16 transposed reads and
 // tile writes), double buffering filled by direct global->LDS loads issued one step ahead, and
 // the softmax scale folded into dS so that dK and dQ need no further multiplies.
-#include <mutex>
-
 #include "kern_common.h"
 
 namespace ra {
@@ -663,26 +661,6 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
 }
 
 }  // namespace
-
-// Scratch of ra_chunk_bwd_ds_noalloc (the stored dS of one call): one copy per GPU, held until the
-// process ends.  Host code never uses this name as an address: noalloc_scratch_address returns
-// the device address of each GPU's copy.
-static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
-
-int noalloc_scratch_address(int device, void** out) {
-  static std::mutex mu;
-  static void* addr[kMaxDevices] = {};
-  if (device < 0 || device >= kMaxDevices) return (int)hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!addr[device]) {
-    void* p = nullptr;  // the calling thread has `device` current
-    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return (int)e;
-    addr[device] = p;
-  }
-  *out = addr[device];
-  return 0;
-}
 
 int launch_chunk_bwd_bf16(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   return kv.D == 128 ? launch_bwd<128>(kv, q, stream, fork) : launch_bwd<64>(kv, q, stream, fork);
