@@ -44,6 +44,23 @@ struct KvCfg {
   static constexpr int QT = kKvBQ * D;  // elements of one Q (or dO) tile
 };
 
+// The V tile of a dK/dV workgroup, loaded once through registers into padded rows of D + 8
+// elements: logical 16-byte chunk L = 2 kk + hh of a row sits at position KK hh + kk, so a lane's
+// B operands of dP (kk = 0 .. KK-1, its lane half hh) are consecutive chunks at immediate offsets
+// from one address, and the 16-byte row padding puts 16 consecutive rows on distinct banks
+// (conflict-free reads).  Rows past the range repeat the last valid row (masked later).
+template <int D>
+__device__ __forceinline__ void load_v_padded(const u16* __restrict__ g, int64_t valid_rows, u16* vt) {
+  constexpr int CH = D / 8, KK = D / 16;
+  const int last = (int)(valid_rows < kKvBN ? valid_rows : kKvBN) - 1;
+#pragma unroll
+  for (int i = 0; i < kKvBN * CH / kNT; ++i) {
+    const int idx = i * kNT + (int)threadIdx.x, r = idx / CH, L = idx % CH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(g + (r < last ? r : last) * D + 8 * L);
+    *reinterpret_cast<u32x4*>(vt + r * (D + 8) + 8 * (KK * (L & 1) + (L >> 1))) = v;
+  }
+}
+
 // Raw lse and delta of the step row that accumulator register (lane & 15) holds in this lane's
 // half (row index clamped into the pair): lanes 16 c .. 16 c + 15 of each 16-lane DPP row hold
 // the 16 values its lanes need, handed out per register by a row broadcast.
@@ -90,9 +107,9 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   // __restrict__ parameter, which lets the compiler prove that those loads do not alias its reads
   // (so it does not wait for them before the step's LDS reads).  One array, not several: with
   // several LDS variables the compiler's LDS lowering replaces the pointer-based alias scopes.
-  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * D + 4 * C::QT];
+  __shared__ __attribute__((aligned(16))) u16 lds[kKvBN * (D + 8) + 4 * C::QT];
   u16* const vt = lds;
-  u16* const qdbuf = lds + kKvBN * D;
+  u16* const qdbuf = lds + kKvBN * (D + 8);
 
   const TileRef tr = map_tile(p, kKvBN);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -106,7 +123,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 
   // The workgroup's V tile, resident in LDS for the whole kernel (rows past the range repeat the
   // last key; those keys are masked).
-  issue_tile<D, kKvBN, 4>(Vg, tr.nrows, vt);
+  load_v_padded<D>(Vg, tr.nrows, vt);
   // B operand of S = Q K^T: lane holds K[key][kk*16 + 8*hh .. +8].
   bf16x8 kreg[C::KK];
 #pragma unroll
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
   }
 
   const RowAddr qa = make_row_addr(perm32(lq), hh, D);  // Q / dO rows in perm32 order
-  const RowAddr va = make_row_addr(kl, hh, D);          // this lane's V row
+  const int vrow = kl * (D + 8) + 8 * C::KK * hh;        // this lane's V row (padded layout)
   const TrAddr ta = make_tr_addr(lane, D);              // Q^T, dO^T out of the [query][d] tiles
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
@@ -179,7 +196,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
           s = mfma32(row_operand(Qs, qa, kk), kreg[kk], s);
-          dp = mfma32(row_operand(dOs, qa, kk), row_operand(Vs, va, kk), dp);
+          dp = mfma32(row_operand(dOs, qa, kk), *reinterpret_cast<const bf16x8*>(Vs + vrow + 8 * kk), dp);
         }
         // Excluded (key, query) pairs: keys past the range, and keys after the query in a
         // diagonal pair.  Only steps on an edge take the masked path.
