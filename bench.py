@@ -133,7 +133,7 @@ def chunk_launches(api, prob, wl, k_ring, v_ring):
 # Algorithmic FLOPs of each chunk kernel per unit of counted forward FLOPs (the metric's method
 # work): the forward does Q K^T and P V (1); the dK/dV kernel S, dP, dV and dK (2); the dQ kernel
 # of the rank views forms dQ from the stored dS (0.5).  Together: the backward's 2.5.
-KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_kernel": 2.0, "chunk_bwd_dq_ds_kernel": 0.5}
+KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_pp_kernel": 2.0, "chunk_bwd_dq_ds_kernel": 0.5}
 
 
 def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
@@ -153,7 +153,7 @@ def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
         nbytes = max(api.ra_chunk_bwd_ds_size(prob, chunk, chunk, L[1]) for L in launches)
         scratch = torch.empty(max(16, nbytes), dtype=torch.uint8, device="cuda")
         b = lambda L: bufs[L[0]]
-        run["chunk_bwd_kv_kernel"] = lambda L: api.ra_chunk_bwd_ds(
+        run["chunk_bwd_kv_pp_kernel"] = lambda L: api.ra_chunk_bwd_ds(
             ctx, prob, b(L)["q"], b(L)["do"], b(L)["lse"], delta[L[0]], L[2], L[3], L[1], None, dk, dv,
             scratch, stream)
         run["chunk_bwd_dq_ds_kernel"] = lambda L: api.ra_chunk_bwd_ds(

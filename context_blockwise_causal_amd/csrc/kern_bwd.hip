@@ -37,6 +37,17 @@ constexpr int kNT = 256;
 constexpr int kKvBN = 128;  // keys per workgroup
 constexpr int kKvBQ = 32;   // query rows per step
 
+// Stored scale * dS^T (bf16) of one pair and (batch, query head): ds_rows keys x ds_ld queries
+// in blocks of 32 keys x 32 queries, each 2 KB and contiguous; block (key / 32, query / 32) at
+// element (key / 32) * 32 ds_ld + (query / 32) * 1024, and inside a block key k, query
+// 16 c + 8 h + e at 512 c + 16 k + 8 h + e.  A dK/dV wavefront's step (32 keys x 32 queries; lane
+// (k, h) holds queries 16 c + 8 h .. +7 of key k for c = 0, 1) is then two fully coalesced 1 KB
+// stores, and 8 queries of one key are 16 contiguous bytes for the dQ pass.
+__device__ __forceinline__ int64_t ds_block_off(int64_t key, int64_t q, int64_t ld) {
+  return (key >> 5) * 32 * ld + (q >> 5) * 1024 + ((q >> 4) & 1) * 512 + (key & 31) * 16 + ((q >> 3) & 1) * 8 +
+         (q & 7);
+}
+
 template <int D>
 struct KvCfg {
   static constexpr int KK = D / 16;
@@ -49,13 +60,13 @@ struct KvCfg {
 // B operands of dP (kk = 0 .. KK-1, its lane half hh) are consecutive chunks at immediate offsets
 // from one address, and the 16-byte row padding puts 16 consecutive rows on distinct banks
 // (conflict-free reads).  Rows past the range repeat the last valid row (masked later).
-template <int D>
+template <int D, int ROWS, int NT>
 __device__ __forceinline__ void load_v_padded(const u16* __restrict__ g, int64_t valid_rows, u16* vt) {
   constexpr int CH = D / 8, KK = D / 16;
-  const int last = (int)(valid_rows < kKvBN ? valid_rows : kKvBN) - 1;
+  const int last = (int)(valid_rows < ROWS ? valid_rows : ROWS) - 1;
 #pragma unroll
-  for (int i = 0; i < kKvBN * CH / kNT; ++i) {
-    const int idx = i * kNT + (int)threadIdx.x, r = idx / CH, L = idx % CH;
+  for (int i = 0; i < ROWS * CH / NT; ++i) {
+    const int idx = i * NT + (int)threadIdx.x, r = idx / CH, L = idx % CH;
     const u32x4 v = *reinterpret_cast<const u32x4*>(g + (r < last ? r : last) * D + 8 * L);
     *reinterpret_cast<u32x4*>(vt + r * (D + 8) + 8 * (KK * (L & 1) + (L >> 1))) = v;
   }
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 
   // The workgroup's V tile, resident in LDS for the whole kernel (rows past the range repeat the
   // last key; those keys are masked).
-  load_v_padded<D>(Vg, tr.nrows, vt);
+  load_v_padded<D, kKvBN, kNT>(Vg, tr.nrows, vt);
   // B operand of S = Q K^T: lane holds K[key][kk*16 + 8*hh .. +8].
   bf16x8 kreg[C::KK];
 #pragma unroll
@@ -167,10 +178,11 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
     const float* lsep = p.lse + qhead + pr.q_row0;
     const float* dltp = p.delta + qhead + pr.q_row0;
-    // Stored scale * dS^T (bf16, key-major: ds_rows keys of ds_ld queries) of this (batch, query
-    // head) and pair, at this lane's key row.
+    // Stored scale * dS^T (bf16, 32 x 32 blocks, see ds_block_off) of this (batch, query head)
+    // and pair: the block row of this wavefront's 32 keys, and this lane's place in a block.
     u16* const dsp = DS ? reinterpret_cast<u16*>(p.ds) + pr.ds_off +
-                              (((int64_t)tr.b * p.Hq + tr.hq) * pr.ds_rows + kloc0 + kl) * pr.ds_ld
+                              (((int64_t)tr.b * p.Hq + tr.hq) * pr.ds_rows + kloc0 + 32 * w) * pr.ds_ld +
+                              16 * lq + 8 * hh
                         : nullptr;
     // One query step on (Qs, dOs); the next step's rows go into (nQ, ndO).
     // (la, ld): raw lse / delta of this step's rows, loaded one step ahead.
@@ -237,16 +249,15 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
           dsb[c] = b;
         }
         // scale * dS (bf16, exactly the operand of dK) for the dQ pass: registers 8c .. 8c+7 of
-        // this lane are queries 16 c + 8 hh .. +7 of the step at its key, i.e. 16 contiguous bytes
-        // of the key's dS^T row.  Key rows past the range (the block has 128-row granules) and
-        // query columns past the pair (up to ds_ld) get values that nothing reads.  The two halves
-        // of a 64-byte row segment come from the two lane halves of one instruction, and the next
-        // step fills the rest of the cache line.  The stores go out ahead of the dV / dK
-        // contractions, which give them time to complete before the wait that ends the step.
+        // this lane are queries 16 c + 8 hh .. +7 of the step at its key, so the wavefront's step
+        // is one 32 x 32 block, two 1 KB stores.  Key rows past the range (the block has 128-row
+        // granules) and query columns past the pair (up to ds_ld) get values that nothing reads.
+        // The stores go out ahead of the dV / dK contractions, which give them time to complete
+        // before the wait that ends the step.
         if (DS) {
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            *reinterpret_cast<bf16x8*>(dsp + qbase + 16 * c + 8 * hh) = dsb[c];
+            *reinterpret_cast<bf16x8*>(dsp + qbase * 32 + 512 * c) = dsb[c];
           __builtin_amdgcn_sched_barrier(0);
         }
         // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed out of the tiles.
@@ -303,6 +314,367 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
         unsafeAtomicAdd(g + k * D + d, st[k * D + (((d >> 2) ^ (k & 15)) << 2) + (d & 3)]);
       }
     }
+  }
+}
+
+// ======================================================================= dK / dV, ping-pong
+//
+// The same computation with two teams of 4 wavefronts per workgroup (8 wavefronts, two per
+// SIMD, one of each team), each team owning 128 keys; both teams walk the same query steps and
+// share their Q / dO / lse / delta tiles.  A wavefront's step is split into a matrix phase (the
+// dV / dK contractions of the previous step and the S / dP contractions of this step) and a
+// vector phase (P and dS of this step).  The teams run these phases half a step apart, separated
+// by workgroup barriers, so that on every SIMD one wavefront issues MFMAs while the other does its
+// exponentials and conversions: the matrix core does not wait for the vector work of the
+// wavefront it serves.  The tiles rotate through three LDS buffers; the first team loads step
+// t + 1 during its matrix phase of step t, and its vector phase waits for those loads.
+
+constexpr int kPPKeys = 256;  // keys per workgroup (two teams of 128)
+constexpr int kBufRsrcWord3 = 0x00020000;  // buffer resource word 3 (gfx9 family): raw 32-bit data
+constexpr int kPPNT = 512;    // threads per workgroup
+
+// Barrier between two phases of the ping-pong kernel.  The only data the wavefronts share inside
+// the phase loop are LDS tiles written by direct loads whose issuer waits for them (vmcnt) before
+// the barrier that publishes them, and LDS tiles read by MFMA operand loads that must be done
+// before a later phase overwrites them: this waits for the wavefront's LDS reads only, not for its
+// dS stores or its lse / delta loads in flight (which a fence-carrying barrier would).  The empty
+// asm with a memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool DS>
+__global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams p) {
+  using C = KvCfg<D>;
+  constexpr int BUF = 2 * C::QT + 128;  // Q tile, dO tile, then 32 lse and 32 delta values (fp32)
+  constexpr int VP = D + 8;             // padded V row
+  constexpr int STG = 4 * 1024;         // the first team's scale * dS of one step (4 x 64 lanes x 32 B)
+  __shared__ __attribute__((aligned(16))) u16 lds[kPPKeys * VP + 4 * BUF + (DS ? STG : 0)];
+  u16* const vt = lds;
+  u16* const tiles = lds + kPPKeys * VP;
+  u16* const stg = tiles + 4 * BUF;
+
+  const TileRef tr = map_tile(p, kPPKeys);
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int team = w >> 2, kw = 32 * w;  // kw: the wavefront's first key within the tile
+  const int kl = kw + lq;                // this lane's key within the tile
+  const bool kvalid = kl < tr.nrows, wvalid = kw < tr.nrows;
+  const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
+  const int64_t qhead = ((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows;
+  const int64_t dkvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.dkv_head_rows;
+  const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k) + (kvhead + tr.row0) * D;
+  const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v) + (kvhead + tr.row0) * D;
+
+  load_v_padded<D, kPPKeys, kPPNT>(Vg, tr.nrows, vt);
+  bf16x8 kreg[C::KK];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+    kreg[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Kg + kl * D + kk * 16 + 8 * hh)
+                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    dk_acc[db] = f32x16{};
+    dv_acc[db] = f32x16{};
+  }
+  const RowAddr qa = make_row_addr(perm32(lq), hh, D);
+  const int vrow = kl * VP + 8 * C::KK * hh;
+  const TrAddr ta = make_tr_addr(lane, D);
+  const float l2s = __builtin_amdgcn_logf(p.scale);  // log2(scale)
+
+  const KRange& R = p.ranges[tr.range];
+  for (int pi = 0; pi < R.npairs; ++pi) {
+    const KPair pr = p.pairs[R.pair[pi]];
+    const bool diag = pr.mask == RA_MASK_DIAG;
+    const int64_t kloc0 = tr.row0 - pr.kv_row0;
+    const int64_t kwave = kloc0 + kw;  // pair-local index of the wavefront's first key
+    const int64_t kj = kwave + lq;
+    const int64_t q_begin = diag ? (kloc0 / kKvBQ) * kKvBQ : 0;
+    const bool has_hi = p.window > 0 || p.attn_chunk > 0;
+    int64_t wave_hi_min = 0, q_end = pr.q_len;
+    int hi32 = 1 << 30;
+    if (has_hi) {
+      const int64_t hi = highest_query(pr.kv_pos0 + kj, p.window, p.attn_chunk) - pr.q_pos0;
+      hi32 = (int)(hi < -1 ? -1 : (hi > pr.q_len ? pr.q_len : hi));
+      wave_hi_min = highest_query(pr.kv_pos0 + kwave, p.window, p.attn_chunk) - pr.q_pos0;
+      const int64_t wg_hi = highest_query(pr.kv_pos0 + kloc0 + tr.nrows - 1, p.window, p.attn_chunk) - pr.q_pos0;
+      if (wg_hi + 1 < q_end) q_end = wg_hi + 1;
+    }
+    const int niter = (int)((q_end - q_begin + kKvBQ - 1) / kKvBQ);
+    if (niter <= 0) continue;
+    const u16* Qp = reinterpret_cast<const u16*>(p.q) + (qhead + pr.q_row0) * D;
+    const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
+    const float* lsep = p.lse + qhead + pr.q_row0;
+    const float* dltp = p.delta + qhead + pr.q_row0;
+    // stored scale * dS^T: the block row of the wavefront's 32 keys (see ds_block_off); only rows
+    // of wavefronts holding a valid key are stored (they lie inside the pair's 128-row granules)
+    char* const dsw = DS ? reinterpret_cast<char*>(reinterpret_cast<u16*>(p.ds) + pr.ds_off +
+                                                   (((int64_t)tr.b * p.Hq + tr.hq) * pr.ds_rows + kwave) * pr.ds_ld)
+                         : nullptr;
+
+    // Carried from one phase to the next: S and dP after a matrix phase; P and scale * dS (bf16,
+    // packed into s) after a vector phase.  One pair of register blocks for both keeps the
+    // values live at the loop head to 32 registers.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    // The first team loads the tiles of the step at row q0 (Q, dO, lse and delta; rows past the
+    // pair repeat its last row) with direct buffer loads: unlike the global form, a buffer load to
+    // LDS in flight leaves the compiler's waits for LDS reads exact.  Each buffer resource spans
+    // the step's rows only.
+    auto load = [&](int64_t q0, u16* __restrict__ B) {
+      const int last = (int)(pr.q_len - q0 < kKvBQ ? pr.q_len - q0 : kKvBQ) - 1;
+      const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(Qp + q0 * D), 0, kKvBQ * D * 2, kBufRsrcWord3);
+      const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(dOp + q0 * D), 0, kKvBQ * D * 2, kBufRsrcWord3);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = k * 4 + w, row = i * 4 + lane / 16;
+        const int c = (lane % 16) ^ swz(row, D);
+        const unsigned off = (unsigned)((row < last ? row : last) * D + c * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lvoid_t*)(B + i * 512), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lvoid_t*)(B + C::QT + i * 512), 16, off, 0, 0, 0);
+      }
+      if (w == 0) {  // lanes 0-31: lse, 32-63: delta of the step's rows
+        const unsigned off = (unsigned)(lq < last ? lq : last) * 4u;
+        // two instructions, each with one half of the lanes active (one resource each)
+        const auto rl = __builtin_amdgcn_make_buffer_rsrc((void*)(lsep + q0), 0, kKvBQ * 4, kBufRsrcWord3);
+        const auto rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dltp + q0), 0, kKvBQ * 4, kBufRsrcWord3);
+        if (hh == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lvoid_t*)(B + 2 * C::QT), 4, off, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (hh == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lvoid_t*)(B + 2 * C::QT), 4, off, 0, 0, 0);
+      }
+    };
+    // One phase of this wavefront for step t: the matrix phase (mph: the dV / dK contractions of
+    // step t - 1 if dvdk, the S / dP contractions of step t if sdp) or the vector phase.  Bc holds
+    // step t's tiles, Bo step t - 1's, B1 step t + 1's and Bn receives step t + 2's (first team,
+    // matrix phase); Sg is the staging area of the first team's dS.
+    auto phase = [&](bool mph, bool dvdk, bool sdp, int t, u16* __restrict__ Bn, const u16* __restrict__ Bo,
+                     const u16* __restrict__ Bc, u16* __restrict__ B1, const u16* __restrict__ Vs,
+                     u16* __restrict__ Sg) {
+      const int64_t qbase = q_begin + (int64_t)t * kKvBQ;
+      if (mph) {
+        __builtin_amdgcn_s_setprio(1);  // the matrix phase's MFMAs go ahead of the other wavefront's vector work
+        if (team == 0 && t + 2 < niter) load(qbase + 2 * kKvBQ, Bn);
+        if (dvdk) {
+          // the per-db addresses are formed here, not kept live across the loop
+          TrAddr tq = ta;
+          asm volatile("" : "+v"(tq.lo), "+v"(tq.hi));
+          const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 0, 1, 2, 3)),
+                                __builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 4, 5, 6, 7))};
+          const bf16x8 dsb[2] = {__builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 8, 9, 10, 11)),
+                                 __builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 12, 13, 14, 15))};
+          __builtin_amdgcn_sched_barrier(0);
+          // dV^T += dO^T P and dK^T += Q^T dS of step t - 1.  The operands of group db + 1 are read
+          // while the MFMAs of group db run (the other wavefront of the SIMD is in its vector phase
+          // and cannot fill the matrix core's gaps).
+          bf16x8 A[2][4];
+          auto load_group = [&](int db, bf16x8* o) {
+            o[0] = tr_operand(Bo + C::QT, tq, D, 0, db);
+            o[1] = tr_operand(Bo, tq, D, 0, db);
+            o[2] = tr_operand(Bo + C::QT, tq, D, 1, db);
+            o[3] = tr_operand(Bo, tq, D, 1, db);
+          };
+          load_group(0, A[0]);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            if (db + 1 < C::DB) load_group(db + 1, A[(db + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8* o = A[db & 1];
+            dv_acc[db] = mfma32(o[0], pb[0], dv_acc[db]);
+            dk_acc[db] = mfma32(o[1], dsb[0], dk_acc[db]);
+            dv_acc[db] = mfma32(o[2], pb[1], dv_acc[db]);
+            dk_acc[db] = mfma32(o[3], dsb[1], dk_acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // the previous step's operands are dead before this step's S and dP accumulators start
+        __builtin_amdgcn_sched_barrier(0);
+        if (sdp) {
+          // S = Q K^T and dP = dO V^T; the Q and dO operands are read two kk ahead, V one ahead
+          bf16x8 qo[3], oo[3], vo[2];
+          RowAddr rq = qa;  // the per-kk addresses are formed here, not kept live across the loop
+          asm volatile("" : "+v"(rq.base), "+v"(rq.g8));
+          auto load_qo = [&](int kk) {
+            qo[kk % 3] = row_operand(Bc, rq, kk);
+            oo[kk % 3] = row_operand(Bc + C::QT, rq, kk);
+          };
+          auto load_v = [&](int kk) { vo[kk & 1] = *reinterpret_cast<const bf16x8*>(Vs + vrow + 8 * kk); };
+          load_qo(0);
+          load_v(0);
+          load_qo(1);
+          s = f32x16{};
+          dp = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < C::KK; ++kk) {
+            if (kk + 2 < C::KK) load_qo(kk + 2);
+            if (kk + 1 < C::KK) load_v(kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            s = mfma32(qo[kk % 3], kreg[kk], s);
+            dp = mfma32(oo[kk % 3], vo[kk & 1], dp);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (DS && team == 1 && kw - 128 < tr.nrows) {
+          // The second team stores scale * dS for the dQ pass, its own (end of the phase) and that
+          // of its partner in the first team (keys 128 lower), staged in LDS in the previous phase.
+          // Registers 8c .. 8c+7 of a lane are queries 16 c + 8 hh .. +7 of the step at its key:
+          // a wavefront's step is one 32 x 32 block (see ds_block_off), two 1 KB stores.  Nothing
+          // waits for these stores.
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const u16* const sp = Sg + (w - 4) * 1024 + ln * 8;
+          const f32x4 x2 = *reinterpret_cast<const f32x4*>(sp), x3 = *reinterpret_cast<const f32x4*>(sp + 512);
+          const unsigned dslane = (unsigned)((ln & 31) * 32 + 16 * (ln >> 5));
+          char* const prow = dsw + (qbase * 32 - 128 * pr.ds_ld) * 2 + dslane;
+          *reinterpret_cast<f32x4*>(prow) = x2;
+          *reinterpret_cast<f32x4*>(prow + 1024) = x3;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // P' = scale P = exp2(scale log2(e) S - L) with L = log2(e) lse - log2(scale) per row
+        // (converted in LDS, +inf past the pair), and scale dS = P' (dP - delta).  Registers
+        // 4j .. 4j+3 of a lane hold 4 consecutive rows: their L and delta are one 16-byte LDS read
+        // each, the same for all lanes of a half.
+        const float* const lf = reinterpret_cast<const float*>(Bc + 2 * C::QT);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rb = ((j >> 1) << 4) | (hh << 3) | ((j & 1) << 2);
+          const f32x4 L = *reinterpret_cast<const f32x4*>(lf + rb);
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(lf + 32 + rb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -L[i]));
+            s[r] = pv;
+            dp[r] = pv * (dp[r] - dl[i]);
+          }
+        }
+        // excluded (key, query) pairs: keys past the range, keys after the query (diagonal pair),
+        // queries past the window / attention chunk of the key
+        const bool edge = !kvalid || (diag && kwave + 31 > qbase) || (has_hi && qbase + kKvBQ - 1 > wave_hi_min);
+        if (edge) {
+          const int qmin = !kvalid ? 1 << 20 : (diag ? (int)(kwave - qbase) + lq : -1);
+          const int qml = qmin - 8 * hh, qmh = hi32 - (int)qbase - 8 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qr = perm_reg_row(r, 0);
+            if (qr < qml || qr > qmh) {
+              s[r] = 0.f;
+              dp[r] = 0.f;
+            }
+          }
+        }
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[c][e] = (__bf16)s[8 * c + e];
+            dsb[c][e] = (__bf16)dp[8 * c + e];
+          }
+        }
+        const f32x4 w0 = __builtin_bit_cast(f32x4, pb[0]), w1 = __builtin_bit_cast(f32x4, pb[1]);
+        const f32x4 w2 = __builtin_bit_cast(f32x4, dsb[0]), w3 = __builtin_bit_cast(f32x4, dsb[1]);
+        s = f32x16{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                   w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
+        if (team == 0) {
+          // Step t + 1's tiles are in LDS before the barrier.  The first team's only memory
+          // operations in flight are its direct loads, which complete in order: after the loads
+          // of step t + 2 (4 instructions; 6 for wavefront 0) leave the wait, those of step t + 1
+          // are done.
+          if (t + 2 < niter)
+            __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+          else
+            wait_vmem();
+          if (w == 0 && t + 1 < niter && lane < 32) {  // step t + 1's L (see the start of the phase)
+            float* const ln = reinterpret_cast<float*>(B1 + 2 * C::QT);
+            ln[lane] = qbase + kKvBQ + lane < pr.q_len ? fmaf(ln[lane], kLog2e, -l2s) : __builtin_inff();
+          }
+          // this wavefront's scale * dS, stored by its partner in the second team
+          if (DS) {
+            u16* const sp = Sg + w * 1024 + lane * 8;
+            *reinterpret_cast<f32x4*>(sp) = w2;
+            *reinterpret_cast<f32x4*>(sp + 512) = w3;
+          }
+        } else if (DS) {
+          // scale * dS for the dQ pass (see the start of the phase)
+          int ln = lane;  // the lane's byte offset in the block is formed here, not kept live
+          asm volatile("" : "+v"(ln));
+          const unsigned dslane = (unsigned)((ln & 31) * 32 + 16 * (ln >> 5));
+          char* const row = dsw + qbase * 64 + dslane;
+          if (wvalid) {
+            *reinterpret_cast<f32x4*>(row) = w2;
+            *reinterpret_cast<f32x4*>(row + 1024) = w3;
+          }
+        }
+      }
+    };
+
+    if (team == 0) {
+      load(q_begin, tiles);
+      if (niter > 1) load(q_begin + kKvBQ, tiles + BUF);
+    }
+    wait_vmem();
+    if (w == 0 && lane < 32) {  // L of step 0 (see the vector phase; step t + 1's is formed in step t's)
+      float* const ln = reinterpret_cast<float*>(tiles + 2 * C::QT);
+      ln[lane] = q_begin + lane < pr.q_len ? fmaf(ln[lane], kLog2e, -l2s) : __builtin_inff();
+    }
+    __syncthreads();
+    auto run = [&](bool mph, bool dvdk, bool sdp, int t) {
+      u16* const Bc = tiles + (t & 3) * BUF;
+      u16* const Bn = tiles + ((t + 2) & 3) * BUF;
+      u16* const Bo = tiles + ((t + 3) & 3) * BUF;
+      u16* const B1 = tiles + ((t + 1) & 3) * BUF;
+      phase(mph, dvdk, sdp, t, Bn, Bo, Bc, B1, vt, stg);
+      phase_barrier();
+    };
+    // Each loop step is the vector phase of step t and the matrix phase of step t + 1 (the first
+    // M has no dV / dK, the last no S / dP).  The second team runs one phase behind the first.
+    if (team == 1) phase_barrier();
+    for (int t = -1; t < niter; ++t) {
+      if (t >= 0) run(false, false, false, t);
+      else phase_barrier();
+      run(true, t >= 0, t + 1 < niter, t + 1);
+    }
+    if (team == 0) phase_barrier();
+  }
+
+  // Epilogue: the teams in turn; each wavefront stages its 32 x D block in LDS and adds it to dk /
+  // dv row by row with fp32 atomics (the query heads of a key/value head add into the same rows).
+  wait_vmem();
+  __syncthreads();
+  float* const st = reinterpret_cast<float*>(lds) + (w & 3) * (32 * D);
+  for (int turn = 0; turn < 2; ++turn) {
+    if (team == turn) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x16* acc = t ? dv_acc : dk_acc;
+        const float f = t ? 1.f / p.scale : 1.f;  // dV was accumulated with scale P
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = 8 * db + 2 * j + hh;
+            *reinterpret_cast<f32x4*>(st + lq * D + ((c ^ (lq & 15)) << 2)) =
+                f32x4{acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
+          }
+        float* const g = (t ? p.dv : p.dk) + (dkvhead + tr.row0 + kw) * D;
+        for (int k = 0; k < 32; ++k) {
+          if (kw + k >= tr.nrows) break;
+#pragma unroll
+          for (int h = 0; h < D / 64; ++h) {
+            const int d = 64 * h + lane;
+            unsafeAtomicAdd(g + k * D + d, st[k * D + (((d >> 2) ^ (k & 15)) << 2) + (d & 3)]);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -484,8 +856,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 
 // ======================================================================= dQ from stored dS
 //
-// The dK/dV kernel writes scale * dS^T (bf16, the operand it feeds to dK) key-major, one row of
-// queries per key.  dQ is then the plain contraction dQ += (scale dS) K: one workgroup = 4
+// The dK/dV kernel writes scale * dS^T (bf16, the operand it feeds to dK) in 32 x 32 blocks (see
+// ds_block_off).  dQ is then the plain contraction dQ += (scale dS) K: one workgroup = 4
 // wavefronts = 128 query rows of one (batch, head), a lane one query; per tile of 64 keys the K
 // tile and the workgroup's 64 x 128 block of dS^T are staged in LDS (direct loads, one tile
 // ahead) and dQ^T += K^T dS^T, with both operands read transposed out of their [key][..] tiles
@@ -500,6 +872,27 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 
 constexpr int kDsBM = 128;  // query rows per workgroup (columns of a dS^T tile)
 constexpr int kDsBN = 64;   // keys per tile (rows of a dS^T tile)
+
+// Issues the direct loads of one 64-key x 128-query dS^T tile (keys key0 .., queries q0 ..; key
+// rows past valid_rows repeat the last valid one) from the blocked layout of one (batch, head)
+// slab S into the swizzled [key][query] LDS tile that the operand reads expect: lane i of
+// instruction j fills LDS row 4 j + i / 16, physical chunk i % 16, i.e. logical chunk
+// (i % 16) ^ swz(row) = 8 queries of one key, which is 16 contiguous bytes of a block.  The 4 keys
+// of one instruction are consecutive, so each (32-query block, 16-query half) it touches is one
+// full 128-byte line.
+__device__ __forceinline__ void issue_ds_tile(const u16* __restrict__ S, int64_t ld, int64_t key0,
+                                              int64_t valid_rows, int64_t q0, u16* tile) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int last = (int)(valid_rows < kDsBN ? valid_rows : kDsBN) - 1;
+#pragma unroll
+  for (int k = 0; k < kDsBN * 16 / 64 / 4; ++k) {
+    const int i = k * 4 + w;
+    const int row = i * 4 + lane / 16;
+    const int cq = (lane % 16) ^ swz(row, kDsBM);
+    const int64_t key = key0 + (row < last ? row : last);
+    g2lds16_nt(S + ds_block_off(key, q0 + 8 * cq, ld), tile + i * 512);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p) {
@@ -534,8 +927,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
     if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
     const int nkt = (int)((key_end + kDsBN - 1) / kDsBN);
     const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
-    // this workgroup's 128 query columns of the pair's dS^T block (rows of ds_ld queries)
-    const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + head * pr.ds_rows * pr.ds_ld + qloc0;
+    // the pair's dS^T slab of this (batch, head); this workgroup reads its 128 query columns
+    const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + head * pr.ds_rows * pr.ds_ld;
     const int64_t wq_first = qloc0 + 32 * w;
     const bool wave_has_rows = 32 * w < tr.nrows;
     const bool has_lo = p.window > 0 || p.attn_chunk > 0;
@@ -553,8 +946,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
       const int64_t kbase = (int64_t)t * kDsBN;
       if (t + 1 < nkt) {
         issue_tile<D, kDsBN, 4>(Kp + (kbase + kDsBN) * D, pr.kv_len - kbase - kDsBN, nk);
-        issue_tile_pitched<kDsBM, kDsBN, 4>(Sp + (kbase + kDsBN) * pr.ds_ld, pr.ds_ld,
-                                            pr.kv_len - kbase - kDsBN, ns);
+        issue_ds_tile(Sp, pr.ds_ld, kbase + kDsBN, pr.kv_len - kbase - kDsBN, qloc0, ns);
       }
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
                           !(has_lo && kbase + kDsBN - 1 < wave_lo);
@@ -597,8 +989,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
 
     if (kt0 >= nkt) continue;  // uniform over the workgroup
     issue_tile<D, kDsBN, 4>(Kp + kt0 * kDsBN * D, pr.kv_len - kt0 * kDsBN, buf);
-    issue_tile_pitched<kDsBM, kDsBN, 4>(Sp + kt0 * kDsBN * pr.ds_ld, pr.ds_ld, pr.kv_len - kt0 * kDsBN,
-                                        buf + KT);
+    issue_ds_tile(Sp, pr.ds_ld, kt0 * kDsBN, pr.kv_len - kt0 * kDsBN, qloc0, buf + KT);
     wait_vmem();
     __syncthreads();
     for (int t = (int)kt0; t < nkt; ++t) {
@@ -628,7 +1019,10 @@ int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFo
   const int64_t nkv = kv.dk ? (int64_t)kv.B * kv.Hq * kv.tiles_per_head : 0;
   const int64_t nq = q.U ? (int64_t)q.B * q.Hq * q.tiles_per_head : 0;
   if (nkv > 0) {
-    hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, true>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
+    if (D == 128)
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, true>), dim3((unsigned)nkv), dim3(kPPNT), 0, (hipStream_t)stream, kv);
+    else
+      hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, true>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   if (nq == 0) return 0;
@@ -663,7 +1057,10 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
     qs = (hipStream_t)fork->side;
   }
   if (do_kv) {
-    hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, false>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
+    if (D == 128)
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, false>), dim3((unsigned)nkv), dim3(kPPNT), 0, (hipStream_t)stream, kv);
+    else
+      hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, false>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
   if (do_q) {

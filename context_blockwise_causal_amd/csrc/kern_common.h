@@ -194,27 +194,6 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t va
   }
 }
 
-// The same for a tile whose global rows are `pitch` elements apart (COLS elements used per row),
-// read once: loaded with the non-temporal policy.
-template <int COLS, int ROWS, int NWAVES>
-__device__ __forceinline__ void issue_tile_pitched(const u16* __restrict__ g, int64_t pitch,
-                                                   int64_t valid_rows, u16* tile) {
-  constexpr int CH = COLS / 8;
-  constexpr int RPI = 64 / CH;
-  constexpr int NI = ROWS / RPI;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  static_assert(NI % NWAVES == 0, "tile rows must split evenly over the wavefronts");
-  const int last = (int)(valid_rows < ROWS ? valid_rows : ROWS) - 1;
-#pragma unroll
-  for (int k = 0; k < NI / NWAVES; ++k) {
-    const int i = k * NWAVES + w;
-    const int row = i * RPI + lane / CH;
-    const int c = (lane % CH) ^ swz(row, COLS);
-    const int64_t off = ((int64_t)(row < last ? row : last) * pitch + c * 8) * 2;  // bytes
-    g2lds16_nt(reinterpret_cast<const char*>(g) + off, tile + i * 512);
-  }
-}
-
 struct TileRef {
   int b, hq, g, range;
   int64_t row0;  // first outer row of the tile (in the operand's rows)

@@ -49,19 +49,19 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     # an earlier layout dispatch gathers a tensor of another size; the calibration is the last one
     fdir = write("f", "FETCH_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 8),
                                      ("ra::layout_kernel(...)", calib / 1024 / 2),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 100.0),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 300.0),
+                                     ("void ra::chunk_bwd_kv_pp_kernel<128, true>(ra::KParams)", 100.0),
+                                     ("void ra::chunk_bwd_kv_pp_kernel<128, true>(ra::KParams)", 300.0),
                                      ("ra::copy2d_kernel(...)", stage / 1024 / 3)])
     wdir = write("w", "WRITE_SIZE", [("ra::layout_kernel(...)", calib / 1024 / 4),
                                      ("ra::layout_kernel(...)", calib / 1024),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
-                                     ("void ra::chunk_bwd_kv_kernel<128>(ra::KParams)", 50.0),
+                                     ("void ra::chunk_bwd_kv_pp_kernel<128, true>(ra::KParams)", 50.0),
+                                     ("void ra::chunk_bwd_kv_pp_kernel<128, true>(ra::KParams)", 50.0),
                                      ("ra::copy2d_kernel(...)", stage / 1024 / 1.5)])
     out = tmp_path / "rec.json"
     monkeypatch.setattr(bench, "traffic_path", lambda name: str(out))
     bench.traffic_summary("wl", fdir, wdir, calib, stage)
     rec = json.load(open(out))
-    k = rec["kernels"]["chunk_bwd_kv_kernel"]
+    k = rec["kernels"]["chunk_bwd_kv_pp_kernel"]
     assert k["fetch_bytes_per_launch"] == pytest.approx(200.0 * 1024 * 2)
     assert k["write_bytes_per_launch"] == pytest.approx(50.0 * 1024)
     assert rec["source_hash"] == bench.source_hash()
