@@ -385,7 +385,8 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
   const RowAddr qa = make_row_addr(perm32(lq), hh, D);
   const int vrow = kl * VP + 8 * C::KK * hh;
   const TrAddr ta = make_tr_addr(lane, D);
-  const float l2s = __builtin_amdgcn_logf(p.scale);  // log2(scale)
+  // log2(scale), wave-uniform (kept in a scalar register)
+  const float l2s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_amdgcn_logf(p.scale))));
 
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
@@ -467,26 +468,28 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
           const bf16x8 dsb[2] = {__builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 8, 9, 10, 11)),
                                  __builtin_bit_cast(bf16x8, __builtin_shufflevector(s, s, 12, 13, 14, 15))};
           __builtin_amdgcn_sched_barrier(0);
-          // dV^T += dO^T P and dK^T += Q^T dS of step t - 1.  The operands of group db + 1 are read
-          // while the MFMAs of group db run (the other wavefront of the SIMD is in its vector phase
-          // and cannot fill the matrix core's gaps).
-          bf16x8 A[2][4];
-          auto load_group = [&](int db, bf16x8* o) {
-            o[0] = tr_operand(Bo + C::QT, tq, D, 0, db);
-            o[1] = tr_operand(Bo, tq, D, 0, db);
-            o[2] = tr_operand(Bo + C::QT, tq, D, 1, db);
-            o[3] = tr_operand(Bo, tq, D, 1, db);
+          // dV^T += dO^T P and dK^T += Q^T dS of step t - 1.  The operands are read well ahead of
+          // their MFMAs (the other wavefront of the SIMD is in its vector phase and cannot fill the
+          // matrix core's gaps).
+          // The 16 MFMAs in the order (db, c): dV += dO^T(c, db) P(c), dK += Q^T(c, db) dS(c); the
+          // A operand of MFMA i is read kWin - 1 MFMAs ahead into a rolling window of registers.
+          constexpr int kWin = 8;
+          bf16x8 A[kWin];
+          auto load_op = [&](int i) {
+            const int db = i >> 2, c = (i >> 1) & 1;
+            A[i % kWin] = tr_operand((i & 1) ? Bo : Bo + C::QT, tq, D, c, db);
           };
-          load_group(0, A[0]);
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            if (db + 1 < C::DB) load_group(db + 1, A[(db + 1) & 1]);
+          for (int i = 0; i < kWin - 1; ++i) load_op(i);
+#pragma unroll
+          for (int i = 0; i < 4 * C::DB; ++i) {
+            if (i + kWin - 1 < 4 * C::DB) load_op(i + kWin - 1);
             __builtin_amdgcn_sched_barrier(0);
-            const bf16x8* o = A[db & 1];
-            dv_acc[db] = mfma32(o[0], pb[0], dv_acc[db]);
-            dk_acc[db] = mfma32(o[1], dsb[0], dk_acc[db]);
-            dv_acc[db] = mfma32(o[2], pb[1], dv_acc[db]);
-            dk_acc[db] = mfma32(o[3], dsb[1], dk_acc[db]);
+            const int db = i >> 2, c = (i >> 1) & 1;
+            if (i & 1)
+              dk_acc[db] = mfma32(A[i % kWin], dsb[c], dk_acc[db]);
+            else
+              dv_acc[db] = mfma32(A[i % kWin], pb[c], dv_acc[db]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -520,21 +523,27 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
       } else {
-        if (DS && team == 1 && kw - 128 < tr.nrows) {
-          // The second team stores scale * dS for the dQ pass, its own (end of the phase) and that
-          // of its partner in the first team (keys 128 lower), staged in LDS in the previous phase.
-          // Registers 8c .. 8c+7 of a lane are queries 16 c + 8 hh .. +7 of the step at its key:
-          // a wavefront's step is one 32 x 32 block (see ds_block_off), two 1 KB stores.  Nothing
-          // waits for these stores.
-          int ln = lane;
-          asm volatile("" : "+v"(ln));
-          const u16* const sp = Sg + (w - 4) * 1024 + ln * 8;
-          const f32x4 x2 = *reinterpret_cast<const f32x4*>(sp), x3 = *reinterpret_cast<const f32x4*>(sp + 512);
-          const unsigned dslane = (unsigned)((ln & 31) * 32 + 16 * (ln >> 5));
-          char* const prow = dsw + (qbase * 32 - 128 * pr.ds_ld) * 2 + dslane;
-          *reinterpret_cast<f32x4*>(prow) = x2;
-          *reinterpret_cast<f32x4*>(prow + 1024) = x3;
-          __builtin_amdgcn_sched_barrier(0);
+        // Reads whose latency the phase's arithmetic hides: the first team waits for step t + 1's
+        // tiles (loaded two phases ago) and wavefront 0 reads their raw lse; the second team reads
+        // its partner's staged dS (see the end of the phase).
+        const bool conv = team == 0 && w == 0 && t + 1 < niter;
+        float* const lnext = reinterpret_cast<float*>(B1 + 2 * C::QT);
+        const bool pstore = DS && team == 1 && kw - 128 < tr.nrows;
+        float lraw = 0.f;
+        f32x4 x2 = f32x4{}, x3 = f32x4{};
+        if (team == 0) {
+          // The first team's only memory operations in flight are its direct loads, which
+          // complete in order: after the loads of step t + 2 (4 instructions; 6 for wavefront 0)
+          // leave the wait, those of step t + 1 are done.
+          if (t + 2 < niter)
+            __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+          else
+            wait_vmem();
+          if (conv && lane < 32) lraw = lnext[lane];
+        } else if (pstore) {
+          const u16* const sp = Sg + (w - 4) * 1024 + lane * 8;
+          x2 = *reinterpret_cast<const f32x4*>(sp);
+          x3 = *reinterpret_cast<const f32x4*>(sp + 512);
         }
         // P' = scale P = exp2(scale log2(e) S - L) with L = log2(e) lse - log2(scale) per row
         // (converted in LDS, +inf past the pair), and scale dS = P' (dP - delta).  Registers
@@ -583,26 +592,21 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
         s = f32x16{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
                    w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
         if (team == 0) {
-          // Step t + 1's tiles are in LDS before the barrier.  The first team's only memory
-          // operations in flight are its direct loads, which complete in order: after the loads
-          // of step t + 2 (4 instructions; 6 for wavefront 0) leave the wait, those of step t + 1
-          // are done.
-          if (t + 2 < niter)
-            __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-          else
-            wait_vmem();
-          if (w == 0 && t + 1 < niter && lane < 32) {  // step t + 1's L (see the start of the phase)
-            float* const ln = reinterpret_cast<float*>(B1 + 2 * C::QT);
-            ln[lane] = qbase + kKvBQ + lane < pr.q_len ? fmaf(ln[lane], kLog2e, -l2s) : __builtin_inff();
-          }
-          // this wavefront's scale * dS, stored by its partner in the second team
+          // step t + 1's L (see above), and this wavefront's scale * dS, which its partner in the
+          // second team stores
+          if (conv && lane < 32)
+            lnext[lane] = lane < (int)(pr.q_len - qbase - kKvBQ) ? fmaf(lraw, kLog2e, -l2s) : __builtin_inff();
           if (DS) {
             u16* const sp = Sg + w * 1024 + lane * 8;
             *reinterpret_cast<f32x4*>(sp) = w2;
             *reinterpret_cast<f32x4*>(sp + 512) = w3;
           }
         } else if (DS) {
-          // scale * dS for the dQ pass (see the start of the phase)
+          // The second team stores scale * dS for the dQ pass: its own and that of its partner in
+          // the first team (keys 128 lower), staged in LDS in the previous phase.  Registers
+          // 8c .. 8c+7 of a lane are queries 16 c + 8 hh .. +7 of the step at its key: a
+          // wavefront's step is one 32 x 32 block (see ds_block_off), two 1 KB stores.  Nothing
+          // waits for these stores.
           int ln = lane;  // the lane's byte offset in the block is formed here, not kept live
           asm volatile("" : "+v"(ln));
           const unsigned dslane = (unsigned)((ln & 31) * 32 + 16 * (ln >> 5));
@@ -610,6 +614,11 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
           if (wvalid) {
             *reinterpret_cast<f32x4*>(row) = w2;
             *reinterpret_cast<f32x4*>(row + 1024) = w3;
+          }
+          if (pstore) {
+            char* const prow = row - 128 * pr.ds_ld * 2;
+            *reinterpret_cast<f32x4*>(prow) = x2;
+            *reinterpret_cast<f32x4*>(prow + 1024) = x3;
           }
         }
       }
