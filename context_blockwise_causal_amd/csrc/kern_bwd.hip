@@ -882,24 +882,24 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 constexpr int kDsBM = 128;  // query rows per workgroup (columns of a dS^T tile)
 constexpr int kDsBN = 64;   // keys per tile (rows of a dS^T tile)
 
-// Issues the direct loads of one 64-key x 128-query dS^T tile (keys key0 .., queries q0 ..; key
-// rows past valid_rows repeat the last valid one) from the blocked layout of one (batch, head)
-// slab S into the swizzled [key][query] LDS tile that the operand reads expect: lane i of
-// instruction j fills LDS row 4 j + i / 16, physical chunk i % 16, i.e. logical chunk
-// (i % 16) ^ swz(row) = 8 queries of one key, which is 16 contiguous bytes of a block.  The 4 keys
-// of one instruction are consecutive, so each (32-query block, 16-query half) it touches is one
-// full 128-byte line.
-__device__ __forceinline__ void issue_ds_tile(const u16* __restrict__ S, int64_t ld, int64_t key0,
-                                              int64_t valid_rows, int64_t q0, u16* tile) {
+// A workgroup's 64-key x 128-query dS^T tile in LDS: its 16 half-blocks (32 keys x 16 queries,
+// 1 KB: key block kb, query block qs = the wavefront that reads it, half c) at half-block
+// h = (4 kb + qs) * 2 + c, each in the global layout (key k, query 8 hh + e at 16 k + 8 hh + e) and
+// padded to 1152 bytes, so that the two query halves a transposed read takes at once sit 32 banks
+// apart.
+constexpr int kDsHalf = 576;  // elements per padded half-block
+
+// Issues the direct loads of one dS^T tile (keys key0 .., queries q0 .. of the slab S of one
+// (batch, head)): each instruction copies one contiguous 1 KB half-block, lane i its 16-byte chunk
+// i.  Keys past the pair (up to the slab's 128-row granule) hold values the masks exclude.
+__device__ __forceinline__ void issue_ds_tile(const u16* __restrict__ S, int64_t ld, int64_t key0, int64_t q0,
+                                              u16* tile) {
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int last = (int)(valid_rows < kDsBN ? valid_rows : kDsBN) - 1;
+  const u16* const blk = S + (key0 >> 5) * 32 * ld + (q0 >> 5) * 1024 + 8 * lane;
 #pragma unroll
-  for (int k = 0; k < kDsBN * 16 / 64 / 4; ++k) {
-    const int i = k * 4 + w;
-    const int row = i * 4 + lane / 16;
-    const int cq = (lane % 16) ^ swz(row, kDsBM);
-    const int64_t key = key0 + (row < last ? row : last);
-    g2lds16_nt(S + ds_block_off(key, q0 + 8 * cq, ld), tile + i * 512);
+  for (int k = 0; k < 4; ++k) {
+    const int h = 4 * w + k, kb = h >> 3, qs = (h >> 1) & 3, c = h & 1;
+    g2lds16_nt(blk + kb * 32 * ld + qs * 1024 + c * 512, tile + h * kDsHalf);
   }
 }
 
@@ -907,7 +907,7 @@ template <int D>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p) {
   constexpr int DB = D / 32;
   constexpr int KT = kDsBN * D;       // elements of one K tile
-  constexpr int ST = kDsBN * kDsBM;   // elements of one dS^T tile (64 keys x 128 queries)
+  constexpr int ST = 16 * kDsHalf;    // elements of one dS^T tile (64 keys x 128 queries, padded)
   // two buffers of (K tile, dS^T tile), read and filled through __restrict__ pointers
   __shared__ __attribute__((aligned(16))) u16 buf[2 * (KT + ST)];
 
@@ -924,7 +924,12 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
   const TrAddr kt = make_tr_addr(lane, D);      // K^T out of the [key][d] tile
-  const TrAddr st = make_tr_addr(lane, kDsBM);  // dS^T columns out of the [key][query] tile
+  // dS^T columns out of the half-blocks: lane j of 16-lane group g addresses key 8 (g >> 1) + j / 4
+  // (+4 for the second read, +16 per odd key step, + one key block per two steps) and queries
+  // 16 (g & 1) + 4 (j % 4) .. +3 of this wavefront's query block
+  const int dsg = lane >> 4, dsj = lane & 15;
+  const int dsaddr = ((4 * 0 + w) * 2 + (dsg & 1)) * kDsHalf + (8 * (dsg >> 1) + (dsj >> 2)) * 16 +
+                     ((dsj & 3) >> 1) * 8 + (dsj & 1) * 4;
   const u16* Kg = reinterpret_cast<const u16*>(p.k);
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
@@ -955,7 +960,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
       const int64_t kbase = (int64_t)t * kDsBN;
       if (t + 1 < nkt) {
         issue_tile<D, kDsBN, 4>(Kp + (kbase + kDsBN) * D, pr.kv_len - kbase - kDsBN, nk);
-        issue_ds_tile(Sp, pr.ds_ld, kbase + kDsBN, pr.kv_len - kbase - kDsBN, qloc0, ns);
+        issue_ds_tile(Sp, pr.ds_ld, kbase + kDsBN, qloc0, ns);
       }
       const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
                           !(has_lo && kbase + kDsBN - 1 < wave_lo);
@@ -963,7 +968,12 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
         // B operand dS^T for key step c: lane holds dS^T[16c + 8hh + e][its query], e = 0..7
         bf16x8 dsb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dsb[c] = tr_operand(sb, st, kDsBM, c, w);
+        for (int c = 0; c < 4; ++c) {
+          const int off = dsaddr + (c >> 1) * 8 * kDsHalf + (c & 1) * 256;
+          const v4i16 lo = ds_read_tr16(sb + off), hi = ds_read_tr16(sb + off + 64);
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          dsb[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         const bool edge = (kbase + kDsBN > pr.kv_len) || (diag && kbase + kDsBN - 1 > wq_first) ||
                           (has_lo && kbase < wave_lo_max);
         if (edge) {
@@ -998,7 +1008,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
 
     if (kt0 >= nkt) continue;  // uniform over the workgroup
     issue_tile<D, kDsBN, 4>(Kp + kt0 * kDsBN * D, pr.kv_len - kt0 * kDsBN, buf);
-    issue_ds_tile(Sp, pr.ds_ld, kt0 * kDsBN, pr.kv_len - kt0 * kDsBN, qloc0, buf + KT);
+    issue_ds_tile(Sp, pr.ds_ld, kt0 * kDsBN, qloc0, buf + KT);
     wait_vmem();
     __syncthreads();
     for (int t = (int)kt0; t < nkt; ++t) {
