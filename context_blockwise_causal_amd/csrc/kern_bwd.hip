@@ -330,23 +330,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_kv_kernel(const KParams p) {
 // t + 1 during its matrix phase of step t, and its vector phase waits for those loads.
 
 constexpr int kPPKeys = 256;  // keys per workgroup (two teams of 128)
-constexpr int kBufRsrcWord3 = 0x00020000;  // buffer resource word 3 (gfx9 family): raw 32-bit data
 constexpr int kPPNT = 512;    // threads per workgroup
-
-// Barrier between two phases of the ping-pong kernel.  The only data the wavefronts share inside
-// the phase loop are LDS tiles written by direct loads whose issuer waits for them (vmcnt) before
-// the barrier that publishes them, and LDS tiles read by MFMA operand loads that must be done
-// before a later phase overwrites them: this waits for the wavefront's LDS reads only, not for its
-// dS stores or its lse / delta loads in flight (which a fence-carrying barrier would).  The empty
-// asm with a memory clobber keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int D, bool DS>
 __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams p) {

@@ -194,6 +194,24 @@ __device__ __forceinline__ void issue_tile(const u16* __restrict__ g, int64_t va
   }
 }
 
+constexpr int kBufRsrcWord3 = 0x00020000;  // buffer resource word 3 (gfx9 family): raw 32-bit data
+
+// Barrier between two phases of a ping-pong kernel (two teams of wavefronts alternating matrix
+// and vector phases).  The only data the wavefronts share inside the phase loop are LDS tiles
+// written by direct loads whose issuer waits for them (vmcnt) before the barrier that publishes
+// them, LDS values written by ds stores, and LDS tiles read by operand loads that must be done
+// before a later phase overwrites them: this waits for the wavefront's LDS operations only, not for
+// its global stores or the direct loads it has in flight (which a fence-carrying barrier would).
+// The empty asm with a memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 struct TileRef {
   int b, hq, g, range;
   int64_t row0;  // first outer row of the tile (in the operand's rows)

@@ -231,11 +231,290 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
   }
 }
 
+// ======================================================================= forward, ping-pong
+//
+// The same computation with two teams of 4 wavefronts per workgroup (8 wavefronts, two per SIMD,
+// one of each team), each team owning 128 query rows; both teams walk the same K/V tiles.  A
+// wavefront's tile is split into a matrix phase (O^T += V^T P^T of the previous tile, then S^T of
+// this tile) and a vector phase (mask, row max, lazy rescale, exp2, row sum, P^T as bf16).  The
+// teams run these phases half a tile apart between workgroup barriers, so that on every SIMD one
+// wavefront issues MFMAs while the other does its softmax.  K/V tiles rotate through four LDS
+// buffers, loaded by the first team two tiles ahead with buffer loads to LDS (which, unlike the
+// global form, leave the compiler's waits for LDS reads exact).
+
+constexpr int kPPRows = 256;  // query rows per workgroup (two teams of 128)
+constexpr int kPPNT = 512;    // threads per workgroup
+
+template <int D>
+__global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p) {
+  using C = FwdCfg<D>;
+  constexpr int BUF = 2 * C::TILE;  // K tile, then V tile
+  __shared__ __attribute__((aligned(16))) u16 lds[4 * BUF];
+
+  const TileRef tr = map_tile(p, kPPRows);
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int team = w >> 2;
+  const int qi = 32 * w + lq;  // this lane's query row within the tile
+  const bool qvalid = qi < tr.nrows;
+  const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
+  const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
+  const u16* __restrict__ Q = reinterpret_cast<const u16*>(p.q);
+  const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k);
+  const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v);
+
+  bf16x8 qreg[C::KK];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) {
+    if (qvalid)
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + kk * 16 + 8 * hh);
+    else
+      qreg[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x16 oacc[C::DB];
+  float m2 = -__builtin_inff(), lsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  if (qvalid && !p.fresh) {
+    m2 = p.m[qrow] * kLog2e;
+    lsum = p.l[qrow];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][4 * j + i] = u[i];
+      }
+  }
+
+  const RowAddr ka0 = make_row_addr(perm32(lq), hh, D);
+  const RowAddr ka1 = make_row_addr(32 + perm32(lq), hh, D);
+  const TrAddr va = make_tr_addr(lane, D);
+  const KRange& R = p.ranges[tr.range];
+  for (int pi = 0; pi < R.npairs; ++pi) {
+    const KPair pr = p.pairs[R.pair[pi]];
+    const bool diag = pr.mask == RA_MASK_DIAG;
+    const int64_t qloc0 = tr.row0 - pr.q_row0;
+    const int64_t iq = qloc0 + qi;
+    int64_t key_end = pr.kv_len;
+    if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
+    const int nkt = (int)((key_end + kBN - 1) / kBN);
+    const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
+    const u16* Vp = Vg + (kvhead + pr.kv_row0) * D;
+    const int64_t wq_first = qloc0 + 32 * w;
+    const bool has_lo = p.window > 0 || p.attn_chunk > 0;
+    int64_t lo = 0, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
+    if (has_lo) {
+      lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo = lowest_key(pr.q_pos0 + wq_first, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 31, p.window, p.attn_chunk) - pr.kv_pos0;
+      const int64_t tile_lo = lowest_key(pr.q_pos0 + qloc0, p.window, p.attn_chunk) - pr.kv_pos0;
+      kt0 = tile_lo > 0 ? tile_lo / kBN : 0;
+    }
+    if (kt0 >= nkt) continue;  // uniform over the workgroup
+    const int niter = nkt - (int)kt0;
+
+    // The first team loads key tile kt (K then V, rows past the pair repeat its last row): 16
+    // one-KB instructions per tile, 8 per wavefront.
+    auto load = [&](int64_t kt, u16* __restrict__ B) {
+      const int64_t k0 = kt * kBN;
+      const int last = (int)(pr.kv_len - k0 < kBN ? pr.kv_len - k0 : kBN) - 1;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + k0 * D), 0, kBN * D * 2, kBufRsrcWord3);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vp + k0 * D), 0, kBN * D * 2, kBufRsrcWord3);
+      constexpr int CH = D / 8, RPI = 64 / CH;
+#pragma unroll
+      for (int k = 0; k < kBN / RPI / 4; ++k) {
+        const int i = k * 4 + w, row = i * RPI + lane / CH;
+        const int c = (lane % CH) ^ swz(row, D);
+        const unsigned off = (unsigned)((row < last ? row : last) * D + c * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lvoid_t*)(B + i * 512), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lvoid_t*)(B + C::TILE + i * 512), 16, off, 0, 0, 0);
+      }
+    };
+
+    // Carried between phases: the scores S^T of the tile after a matrix phase; P^T (bf16, packed
+    // into s[0]) after a vector phase.
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // One phase for tile t (0-based within the pair's tiles from kt0): the matrix phase (mph: the
+    // P V contraction of tile t - 1 if pv, the scores of tile t if sc) or the vector phase.  Bc
+    // holds tile t, Bo tile t - 1, Bn receives tile t + 2 (first team, matrix phase).
+    auto phase = [&](bool mph, bool pv, bool sc, int t, u16* __restrict__ Bn, const u16* __restrict__ Bo,
+                     const u16* __restrict__ Bc) {
+      const int64_t kbase = (kt0 + t) * kBN;
+      if (mph) {
+        __builtin_amdgcn_s_setprio(1);  // the matrix phase's MFMAs go ahead of the other wavefront's vector work
+        if (team == 0 && t + 2 < niter) load(kt0 + t + 2, Bn);
+        if (pv) {
+          // O^T += V^T P^T of tile t - 1: P^T for key step c is registers 8 (c & 1) .. of block c >> 1,
+          // packed as bf16 into s[0]
+          bf16x8 pb[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            pb[c] = __builtin_bit_cast(
+                bf16x8, c == 0 ? __builtin_shufflevector(s[0], s[0], 0, 1, 2, 3)
+                               : c == 1 ? __builtin_shufflevector(s[0], s[0], 4, 5, 6, 7)
+                                        : c == 2 ? __builtin_shufflevector(s[0], s[0], 8, 9, 10, 11)
+                                                 : __builtin_shufflevector(s[0], s[0], 12, 13, 14, 15));
+          TrAddr tv = va;  // the per-db addresses are formed here, not kept live across the loop
+          asm volatile("" : "+v"(tv.lo), "+v"(tv.hi));
+          __builtin_amdgcn_sched_barrier(0);
+          // the 16 MFMAs in the order (c, db) (consecutive ones into different accumulators), the A
+          // operand V^T(c, db) read kWin - 1 MFMAs ahead
+          constexpr int kWin = 8;
+          bf16x8 A[kWin];
+          auto load_op = [&](int i) { A[i % kWin] = tr_operand(Bo + C::TILE, tv, D, i / C::DB, i % C::DB); };
+#pragma unroll
+          for (int i = 0; i < kWin - 1; ++i) load_op(i);
+#pragma unroll
+          for (int i = 0; i < 4 * C::DB; ++i) {
+            if (i + kWin - 1 < 4 * C::DB) load_op(i + kWin - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[i % C::DB] = mfma32(A[i % kWin], pb[i / C::DB], oacc[i % C::DB]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (sc) {
+          // S^T = K Q^T of tile t for its two 32-key blocks; K rows read two kk ahead
+          RowAddr r0 = ka0, r1 = ka1;
+          asm volatile("" : "+v"(r0.base), "+v"(r0.g8), "+v"(r1.base), "+v"(r1.g8));
+          bf16x8 k0o[3], k1o[3];
+          auto load_k = [&](int kk) {
+            k0o[kk % 3] = row_operand(Bc, r0, kk);
+            k1o[kk % 3] = row_operand(Bc, r1, kk);
+          };
+          load_k(0);
+          load_k(1);
+          s[0] = f32x16{};
+          s[1] = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < C::KK; ++kk) {
+            if (kk + 2 < C::KK) load_k(kk + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = mfma32(k0o[kk % 3], qreg[kk], s[0]);
+            s[1] = mfma32(k1o[kk % 3], qreg[kk], s[1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        // the first team's loads of tile t + 1 (issued two phases ago) are in LDS before the
+        // barrier that ends this phase; its only memory operations in flight are its direct loads,
+        // which complete in order (8 instructions per tile)
+        if (team == 0) {
+          if (t + 2 < niter)
+            __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+          else
+            wait_vmem();
+        }
+        // keys past the pair, after this lane's query (diagonal pair) or below its lowest visible
+        // key get -inf (edge tiles only)
+        const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first) ||
+                          (has_lo && kbase < wave_lo_max);
+        if (edge) {
+          const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
+          const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kBN - 1 ? kBN - 1 : lim - kbase));
+          const int kmin = has_lo ? (int)(lo - kbase < 0 ? 0 : (lo - kbase > kBN ? kBN : lo - kbase)) : 0;
+          const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = b * 32 + perm_reg_row(r, 0);
+              if (key > kmh || key < kml) s[b][r] = -__builtin_inff();
+            }
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+        mx = xor32_max(mx) * p.scale_log2;
+        const bool grow = mx > m2 + kLazyLog2;
+        if (__ballot(grow)) {
+          const float mnew = grow ? mx : m2;
+          const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m2 - mnew);
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+          m2 = mnew;
+        }
+        const float nbase = m2 == -__builtin_inff() ? 0.f : -m2;
+        float rs = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[b][r], p.scale_log2, nbase));
+            s[b][r] = e;
+            rs += e;
+          }
+        rs = xor32_sum(rs);
+        lsum += rs;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)s[c >> 1][8 * (c & 1) + e];
+        }
+        const f32x4 w0 = __builtin_bit_cast(f32x4, pb[0]), w1 = __builtin_bit_cast(f32x4, pb[1]);
+        const f32x4 w2 = __builtin_bit_cast(f32x4, pb[2]), w3 = __builtin_bit_cast(f32x4, pb[3]);
+        s[0] = f32x16{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                      w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
+      }
+    };
+    auto run = [&](bool mph, bool pv, bool sc, int t) {
+      u16* const tiles = lds;
+      u16* const Bc = tiles + (t & 3) * BUF;
+      u16* const Bn = tiles + ((t + 2) & 3) * BUF;
+      u16* const Bo = tiles + ((t + 3) & 3) * BUF;
+      phase(mph, pv, sc, t, Bn, Bo, Bc);
+      phase_barrier();
+    };
+
+    if (team == 0) {
+      load(kt0, lds);
+      if (niter > 1) load(kt0 + 1, lds + BUF);
+    }
+    wait_vmem();
+    __syncthreads();
+    // Each loop step is the vector phase of tile t and the matrix phase of tile t + 1 (the first M
+    // has no P V, the last no scores).  The second team runs one phase behind the first.
+    if (team == 1) phase_barrier();
+    for (int t = -1; t < niter; ++t) {
+      if (t >= 0) run(false, false, false, t);
+      else phase_barrier();
+      run(true, t >= 0, t + 1 < niter, t + 1);
+    }
+    if (team == 0) phase_barrier();
+  }
+
+  if (qvalid) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = oacc[db][4 * j + i];
+        *reinterpret_cast<f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh) = u;
+      }
+    if (hh == 0) {
+      p.m[qrow] = m2 * kLn2;
+      p.l[qrow] = lsum;
+    }
+  }
+}
+
 template <int D>
 int launch_fwd(const KParams& kp, void* stream) {
   const int64_t nblk = (int64_t)kp.B * kp.Hq * kp.tiles_per_head;
   if (nblk == 0) return 0;
-  hipLaunchKernelGGL(chunk_fwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), 0, (hipStream_t)stream, kp);
+  if (D == 128)
+    hipLaunchKernelGGL(chunk_fwd_pp_kernel<D>, dim3((unsigned)nblk), dim3(kPPNT), 0, (hipStream_t)stream, kp);
+  else
+    hipLaunchKernelGGL(chunk_fwd_bf16_kernel<D>, dim3((unsigned)nblk), dim3(kNT), 0, (hipStream_t)stream, kp);
   return (int)hipGetLastError();
 }
 

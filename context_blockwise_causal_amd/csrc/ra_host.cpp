@@ -107,7 +107,7 @@ KParams base_params(const Shape& s) {
 
 int run_fwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* stream) {
   if (s.dtype == RA_BF16) {
-    build_ranges(&kp, pairs, n, true, kFwdTileRows);
+    build_ranges(&kp, pairs, n, true, s.D == 128 ? kFwdPPTileRows : kFwdTileRows);
     return kp.nranges ? launch_chunk_fwd_bf16(kp, stream) : 0;
   }
   build_ranges(&kp, pairs, n, true, kF32FwdTileRows);

@@ -163,6 +163,7 @@ int noalloc_scratch_address(int device, void** out);
 int launch_chunk_fwd_f32(const KParams& kp, void* stream);
 int launch_chunk_bwd_f32(const KParams& kp, void* stream);
 constexpr int64_t kFwdTileRows = 128;   // Q rows per forward workgroup (bf16 MFMA kernel)
+constexpr int64_t kFwdPPTileRows = 256; // Q rows per workgroup of the ping-pong forward (D = 128)
 constexpr int64_t kBwdTileRows = 128;   // K/V rows per dK/dV workgroup (bf16 MFMA kernel)
 constexpr int64_t kBwdPPTileRows = 256; // K/V rows per dK/dV workgroup of the ping-pong kernel (D = 128)
 constexpr int64_t kBwdQTileRows = 128;  // Q rows per dQ workgroup (bf16 MFMA kernel)
