@@ -133,7 +133,7 @@ def chunk_launches(api, prob, wl, k_ring, v_ring):
 # Algorithmic FLOPs of each chunk kernel per unit of counted forward FLOPs (the metric's method
 # work): the forward does Q K^T and P V (1); the dK/dV kernel S, dP, dV and dK (2); the dQ kernel
 # of the rank views forms dQ from the stored dS (0.5).  Together: the backward's 2.5.
-KERNEL_UNITS = {"chunk_fwd_bf16_kernel": 1.0, "chunk_bwd_kv_pp_kernel": 2.0, "chunk_bwd_dq_ds_kernel": 0.5}
+KERNEL_UNITS = {"chunk_fwd_pp_kernel": 1.0, "chunk_bwd_kv_pp_kernel": 2.0, "chunk_bwd_dq_ds_kernel": 0.5}
 
 
 def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
@@ -143,7 +143,7 @@ def kernel_runners(api, ctx, prob, wl, bufs, launches, stream, backward):
     chunk = prob.chunk
     U, m, l = api.new_state(prob, chunk)
     api.ra_state_init(ctx, prob, U, m, l)
-    run = {"chunk_fwd_bf16_kernel": lambda L: api.ra_chunk_fwd(
+    run = {"chunk_fwd_pp_kernel": lambda L: api.ra_chunk_fwd(
         ctx, prob, bufs[L[0]]["q"], L[2], L[3], L[1], U, m, l, stream)}
     if backward:
         delta = {r: api.ra_bwd_preprocess(ctx, prob, bufs[r]["o"], bufs[r]["do"]) for r in wl.ranks}
@@ -531,8 +531,8 @@ def main():
     out["roofline"] = roof
     out["kernels"] = kr
     out["hbm_kernels"] = hbm
-    if "chunk_fwd_bf16_kernel" in kr:
-        fk = kr["chunk_fwd_bf16_kernel"]["total_ms_per_pass"]
+    if "chunk_fwd_pp_kernel" in kr:
+        fk = kr["chunk_fwd_pp_kernel"]["total_ms_per_pass"]
         out["staging_overlap"] = {"rank_views_fwd_ms": round(R["fwd_ms"], 4), "chunk_kernels_fwd_ms": fk,
                                   "ratio": round(fk / R["fwd_ms"], 4)}
     if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
