@@ -288,7 +288,6 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
   }
 
   const RowAddr ka0 = make_row_addr(perm32(lq), hh, D);
-  const RowAddr ka1 = make_row_addr(32 + perm32(lq), hh, D);
   const TrAddr va = make_tr_addr(lane, D);
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
@@ -313,6 +312,14 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
     }
     if (kt0 >= nkt) continue;  // uniform over the workgroup
     const int niter = nkt - (int)kt0;
+    // Tiles that take the mask, as bounds on the tile index t (kept in scalar registers): t >= t_hi
+    // when the tile runs past the pair's end or, on a diagonal pair, past this wavefront's first
+    // query; t < t_lo when it starts below the lowest visible key of the wavefront's last query.
+    int64_t kt_hi = pr.kv_len / kBN;
+    if (diag && (wq_first + 1) / kBN < kt_hi) kt_hi = (wq_first + 1) / kBN;
+    const int64_t kt_lo = has_lo && wave_lo_max > 0 ? (wave_lo_max + kBN - 1) / kBN : 0;
+    const int t_hi = (int)(kt_hi - kt0 < niter ? kt_hi - kt0 : niter);
+    const int t_lo = (int)(kt_lo - kt0 > 0 ? kt_lo - kt0 : 0);
 
     // The first team loads key tile kt (K then V, rows past the pair repeat its last row): 16
     // one-KB instructions per tile, 8 per wavefront.
@@ -376,12 +383,14 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
         __builtin_amdgcn_sched_barrier(0);
         if (sc) {
           // S^T = K Q^T of tile t for its two 32-key blocks; K rows read two kk ahead
-          RowAddr r0 = ka0, r1 = ka1;
-          asm volatile("" : "+v"(r0.base), "+v"(r0.g8), "+v"(r1.base), "+v"(r1.g8));
+          // (rows r and r + 32 share their swizzle: the second row is an immediate offset away)
+          RowAddr r0 = ka0;
+          asm volatile("" : "+v"(r0.base), "+v"(r0.g8));
           bf16x8 k0o[3], k1o[3];
           auto load_k = [&](int kk) {
-            k0o[kk % 3] = row_operand(Bc, r0, kk);
-            k1o[kk % 3] = row_operand(Bc, r1, kk);
+            const u16* const a = Bc + r0.base + ((16 * kk) ^ r0.g8);
+            k0o[kk % 3] = *reinterpret_cast<const bf16x8*>(a);
+            k1o[kk % 3] = *reinterpret_cast<const bf16x8*>(a + 32 * D);
           };
           load_k(0);
           load_k(1);
@@ -410,9 +419,7 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
         }
         // keys past the pair, after this lane's query (diagonal pair) or below its lowest visible
         // key get -inf (edge tiles only)
-        const bool edge = (kbase + kBN > pr.kv_len) || (diag && kbase + kBN - 1 > wq_first) ||
-                          (has_lo && kbase < wave_lo_max);
-        if (edge) {
+        if (t >= t_hi || t < t_lo) {
           const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
           const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kBN - 1 ? kBN - 1 : lim - kbase));
           const int kmin = has_lo ? (int)(lo - kbase < 0 ? 0 : (lo - kbase > kBN ? kBN : lo - kbase)) : 0;
