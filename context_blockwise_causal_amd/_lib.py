@@ -17,6 +17,7 @@ RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
 RA_MASK_FULL, RA_MASK_DIAG, RA_MASK_SKIP = 0, 1, 2
 RA_A2A_SEQ_PACK, RA_A2A_HEAD_UNPACK, RA_A2A_HEAD_PACK, RA_A2A_SEQ_UNPACK = 0, 1, 2, 3
 RA_NOALLOC_SCRATCH_BYTES = 64 << 20  # size of the static scratch of ra_chunk_bwd_ds_noalloc
+RA_DEBUG_POISON_SLOTS, RA_DEBUG_ROCTX = 1, 2  # ra_set_debug flags
 
 
 class ra_problem(ctypes.Structure):
@@ -59,6 +60,7 @@ SIGNATURES = {
     "ra_plan_step": [_PROB, _I32, _I32, ctypes.POINTER(_I32), _PAIRS, ctypes.POINTER(_I32)],
     "ra_workspace_size": [_PROB, _I32, ctypes.POINTER(ctypes.c_size_t)],
     "ra_create": [_I32, ctypes.POINTER(_P)],
+    "ra_set_debug": [_P, ctypes.c_uint32],
     "ra_layout_gather": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
     "ra_layout_scatter": [_P, _PROB, _I32, _I32, _I64, _P, _P, _P],
     "ra_ulysses_reshard": [_P, _PROB, _I32, _I64, _P, _P, _P],

@@ -87,6 +87,10 @@ class Context:
         self.handle = h
         self.device = device
 
+    def set_debug(self, flags: int):
+        """ra_set_debug: L.RA_DEBUG_POISON_SLOTS | L.RA_DEBUG_ROCTX, or 0."""
+        L.call("ra_set_debug", self.handle, flags)
+
     def close(self):
         if self.handle:
             L.load().ra_destroy(self.handle)

@@ -955,7 +955,6 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
         for (int c = 0; c < 4; ++c) {
           const int off = dsaddr + (c >> 1) * 8 * kDsHalf + (c & 1) * 256;
           const v4i16 lo = ds_read_tr16(sb + off), hi = ds_read_tr16(sb + off + 64);
-          typedef short v8i16 __attribute__((ext_vector_type(8)));
           dsb[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
         const bool edge = (kbase + kDsBN > pr.kv_len) || (diag && kbase + kDsBN - 1 > wq_first) ||

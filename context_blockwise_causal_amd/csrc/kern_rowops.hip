@@ -273,6 +273,15 @@ __global__ __launch_bounds__(kThreads) void zero2d_kernel(u32x4* __restrict__ ds
     dst[b * pitch_vec + i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// Fills blocks x nvec 16-byte vectors spaced pitch_vec apart with one 32-bit word.
+__global__ __launch_bounds__(kThreads) void fill2d_kernel(u32x4* __restrict__ dst, long long pitch_vec,
+                                                          long long nvec, unsigned word) {
+  const long long b = blockIdx.y;
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+    dst[b * pitch_vec + i] = u32x4{word, word, word, word};
+}
+
 // Casts blocks x nvec groups of 4 fp32 values to the output dtype; source and destination
 // blocks are pitch4 groups of 4 elements apart.  grid.y walks the blocks.
 template <bool BF16>
@@ -439,6 +448,15 @@ int launch_zero2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t b
   if (nvec == 0 || blocks == 0) return 0;
   hipLaunchKernelGGL(zero2d_kernel, dim3((unsigned)grid2d_x(nvec, blocks), (unsigned)blocks), dim3(kThreads), 0,
                      (hipStream_t)stream, (u32x4*)dst, (long long)(pitch_bytes / 16), nvec);
+  return (int)hipGetLastError();
+}
+
+int launch_fill2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t blocks, uint32_t word,
+                  void* stream) {
+  const long long nvec = block_bytes / 16;
+  if (nvec == 0 || blocks == 0) return 0;
+  hipLaunchKernelGGL(fill2d_kernel, dim3((unsigned)grid2d_x(nvec, blocks), (unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (u32x4*)dst, (long long)(pitch_bytes / 16), nvec, (unsigned)word);
   return (int)hipGetLastError();
 }
 

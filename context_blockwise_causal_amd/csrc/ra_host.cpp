@@ -9,9 +9,13 @@
 // previous step computes on the compute stream.  Event slot_ready[s] orders "copy into slot s"
 // before "compute from slot s"; event slot_free[s] orders "compute from slot s" before the next
 // copy into it.
+#include <dlfcn.h>
 #include <hip/hip_runtime_api.h>
 
+#include <cstdarg>
+#include <cstdio>
 #include <initializer_list>
+#include <mutex>
 
 #include "ra_internal.h"
 
@@ -33,6 +37,8 @@ struct ra_context {
   hipEvent_t ajoin;            // the ring's second compute stream has finished
   hipEvent_t dslocal;          // the backward's local-step dQ kernel has read its dS buffer
   void* noalloc_scratch;       // this device's static scratch (ra_chunk_bwd_ds_noalloc)
+  hipEvent_t poisoned;         // the end-of-ring slot poisoning has been enqueued (debug mode)
+  uint32_t debug;              // RA_DEBUG_* flags
 };
 
 namespace ra {
@@ -66,6 +72,49 @@ struct DeviceGuard {
   ~DeviceGuard() {
     if (prev >= 0) (void)hipSetDevice(prev);
   }
+};
+
+// roctx ranges (RA_DEBUG_ROCTX): the marker library is opened on first use, so that the library
+// has no link-time dependency on it; without it the ranges are no-ops.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static Roctx r;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (const char* name : {"librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"}) {
+      void* h = dlopen(name, RTLD_NOW | RTLD_LOCAL);
+      if (!h) continue;
+      r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+      r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+      if (r.push && r.pop) return;
+      r.push = nullptr;
+      r.pop = nullptr;
+    }
+  });
+  return r;
+}
+
+// A roctx range from construction to destruction (when `on` and the library is there).
+struct Range {
+  bool on = false;
+  Range(bool enable, const char* fmt, ...) {
+    if (!enable || !roctx().push) return;
+    char msg[96];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    on = roctx().push(msg) >= 0;
+  }
+  ~Range() {
+    if (on) (void)roctx().pop();
+  }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
 };
 
 ra_status dev_err(int e, const char* what) {
@@ -175,15 +224,20 @@ int staged_steps(const Shape& s, int32_t rank) {
 
 // The ring loop shared by both passes.  `step_fn(stream, slot, kv_k, kv_v, kv_head_rows, owner,
 // pairs, n)` (slot -1 for the local step) enqueues one step's compute on `stream` and, when `side`
-// is not NULL, part of it on
-// `side`, which the caller joins after the loop.  With `alt` set, the steps staged in slot 1 run
-// on `alt` instead of the compute stream (only for steps that do not depend on each other); the
-// loop joins `alt` into the compute stream before it returns.  A slot is refilled only once all
-// the work that reads it has finished.
+// is not NULL, part of it on `side`, which the caller joins after the loop.  With `alt` set, the
+// steps staged in slot 1 run on `alt` instead of the compute stream (only for steps that do not
+// depend on each other); the loop joins `alt` into the compute stream before it returns.  A slot
+// is refilled only once all the work that reads it has finished.  Debug flags of the context:
+// RA_DEBUG_POISON_SLOTS fills a slot with NaN on the staging stream once that work has finished
+// (before each refill, and both slots after the last step, joined into the compute stream);
+// RA_DEBUG_ROCTX marks the loop and each step with roctx ranges named after `pass`.
 template <class StepFn>
-ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k_ring,
+ra_status ring_loop(ra_context* ctx, const char* pass, const Shape& s, int32_t rank, const void* k_ring,
                     const void* v_ring, char* slot0, char* slot1, hipStream_t cs, hipStream_t ss,
                     hipStream_t side, hipStream_t alt, StepFn step_fn) {
+  const bool poison = (ctx->debug & RA_DEBUG_POISON_SLOTS) != 0;
+  const bool marks = (ctx->debug & RA_DEBUG_ROCTX) != 0;
+  Range loop_range(marks, "ra %s rank %d ring", pass, (int)rank);
   struct Step { int32_t i, owner, n; ra_pair pairs[4]; };
   Step staged[64];
   int nstaged = 0;
@@ -207,12 +261,15 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   const int64_t slot_half = s.B * s.Hkv * chunk_bytes;   // K part of a slot; V follows
   char* slots[2] = {slot0, slot1};
   int e;
+  // NaN as bf16 pairs and as fp32 words
+  auto fill_nan = [&](int sl) { return launch_fill2d(slots[sl], 0, 2 * slot_half, 1, 0x7FC07FC0u, ss); };
 
   auto issue_copy = [&](int k) -> ra_status {
     const int sl = k & 1;
     if (k >= 2 && (e = (int)hipStreamWaitEvent(ss, ctx->freed[sl], 0))) return dev_err(e, "wait slot_free");
     if (k >= 2 && side && (e = (int)hipStreamWaitEvent(ss, ctx->qfreed[sl], 0)))
       return dev_err(e, "wait slot_free (side)");
+    if (k >= 2 && poison && (e = fill_nan(sl))) return dev_err(e, "poison slot");
     if ((e = stage_copy(s, staged[k].owner, k_ring, v_ring, slots[sl], ss))) return dev_err(e, "staging copy");
     if ((e = (int)hipEventRecord(ctx->ready[sl], ss))) return dev_err(e, "record slot_ready");
     return RA_OK;
@@ -231,12 +288,14 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
   }
   if (nstaged > 0 && (st = issue_copy(0)) != RA_OK) return st;
   if (have_local) {
+    Range r(marks, "ra %s step 0 owner %d (local)", pass, (int)local.owner);
     const int64_t off = (int64_t)rank * chunk_bytes;
     if ((e = step_fn(cs, -1, (const char*)k_ring + off, (const char*)v_ring + off, s.S, local.owner,
                      local.pairs, local.n)))
       return dev_err(e, "chunk kernel (local step)");
   }
   for (int k = 0; k < nstaged; ++k) {
+    Range r(marks, "ra %s step %d owner %d (slot %d)", pass, (int)staged[k].i, (int)staged[k].owner, k & 1);
     if (k + 1 < nstaged && (st = issue_copy(k + 1)) != RA_OK) return st;
     const int sl = k & 1;
     const hipStream_t t = kvs[sl];
@@ -251,6 +310,19 @@ ra_status ring_loop(ra_context* ctx, const Shape& s, int32_t rank, const void* k
     alt_join.armed = false;
     if ((e = (int)hipEventRecord(ctx->ajoin, alt))) return dev_err(e, "record alt join");
     if ((e = (int)hipStreamWaitEvent(cs, ctx->ajoin, 0))) return dev_err(e, "wait alt join");
+  }
+  if (poison && nstaged > 0) {
+    // both slots after their last readers; the compute stream (the caller's) then waits for the
+    // fills, so that they are ordered before whatever the caller does with the workspace next
+    for (int sl = 0; sl < (nstaged > 1 ? 2 : 1); ++sl) {
+      if ((e = (int)hipStreamWaitEvent(ss, ctx->freed[sl], 0))) return dev_err(e, "wait slot_free");
+      if (side && (e = (int)hipStreamWaitEvent(ss, ctx->qfreed[sl], 0))) return dev_err(e, "wait slot_free (side)");
+      if ((e = fill_nan(sl))) return dev_err(e, "poison slot");
+    }
+    if (ss != cs) {
+      if ((e = (int)hipEventRecord(ctx->poisoned, ss))) return dev_err(e, "record poison");
+      if ((e = (int)hipStreamWaitEvent(cs, ctx->poisoned, 0))) return dev_err(e, "wait poison");
+    }
   }
   return RA_OK;
 }
@@ -278,6 +350,7 @@ void release(ra_context* c) {
   ev(c->fin);
   ev(c->bfork);
   ev(c->bjoin);
+  ev(c->poisoned);
   for (int i = 0; i < kPoolStreams; ++i)
     if (c->pool[i]) (void)hipStreamDestroy(c->pool[i]);
   delete c;
@@ -314,6 +387,7 @@ ra_status ra_create(int32_t device, ra_context** out) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fin, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->bfork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->bjoin, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->poisoned, hipEventDisableTiming);
   for (int i = 0; i < kPoolStreams && e == hipSuccess; ++i)
     e = hipStreamCreateWithFlags(&c->pool[i], hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -333,6 +407,15 @@ void ra_destroy(ra_context* c) {
   if (!c) return;
   DeviceGuard g(c->device);
   release(c);
+}
+
+ra_status ra_set_debug(ra_context* ctx, uint32_t flags) {
+  clear_error();
+  if (!ctx) return fail(RA_ERR_INVALID, "context is NULL");
+  if (flags & ~(uint32_t)(RA_DEBUG_POISON_SLOTS | RA_DEBUG_ROCTX))
+    return fail(RA_ERR_INVALID, "unknown debug flags 0x%x", (unsigned)flags);
+  ctx->debug = flags;
+  return RA_OK;
 }
 
 ra_status ra_layout_gather(ra_context* ctx, const ra_problem* prob, int32_t rank_begin,
@@ -637,7 +720,7 @@ ra_status ra_rank_view_fwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     kp.dkv_head_rows = kv_head_rows;
     return run_fwd(s, kp, pairs, n, t);
   };
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr,
+  if ((st = ring_loop(ctx, "fwd", s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, nullptr,
                       two ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
   if (two)
@@ -809,7 +892,7 @@ ra_status ra_rank_view_bwd(ra_context* ctx, const ra_problem* prob, int32_t rank
     return launch_cast2d(dvo, static_cast<char*>(dv_ring) + off, pitch, blk, nkvh, s.dtype, t);
   };
   // (the fp32 path adds dQ inside its single kernel: its steps stay on one stream)
-  if ((st = ring_loop(ctx, s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side,
+  if ((st = ring_loop(ctx, "bwd", s, rank, k_ring, v_ring, ws + W.slot[0], ws + W.slot[1], cs, ss, side,
                       s.dtype == RA_BF16 ? ctx->pool[1] : nullptr, step)) != RA_OK)
     return st;
   side_join.armed = false;

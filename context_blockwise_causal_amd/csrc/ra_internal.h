@@ -195,6 +195,9 @@ int launch_cast_from_f32(int64_t n, int32_t dtype, const float* src, void* dst, 
 int launch_fill_zero(int64_t n_floats, float* dst, void* stream);
 // `blocks` blocks of block_bytes (a multiple of 16) zeroed, pitch_bytes apart.
 int launch_zero2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t blocks, void* stream);
+// Fills blocks x block_bytes (a multiple of 16) spaced pitch_bytes apart with one 32-bit word.
+int launch_fill2d(void* dst, int64_t pitch_bytes, int64_t block_bytes, int64_t blocks, uint32_t word,
+                  void* stream);
 // `blocks` blocks of `block` fp32 values (a multiple of 4) cast to dtype; source and destination
 // blocks start `pitch` elements apart.
 int launch_cast2d(const float* src, void* dst, int64_t pitch, int64_t block, int64_t blocks, int32_t dtype,

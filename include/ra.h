@@ -137,6 +137,22 @@ ra_status ra_workspace_size(const ra_problem* problem, int32_t pass, size_t* byt
 ra_status ra_create(int32_t device, ra_context** out);
 void ra_destroy(ra_context* ctx);
 
+/* Debugging aids of a context: flags (0 when the context is created, the production setting).
+ * RA_DEBUG_POISON_SLOTS: the rank views (ra_rank_view_fwd, ra_rank_view_bwd) fill a staging slot
+ *   with NaN on the staging stream as soon as the work that reads it has finished, i.e. after its
+ *   slot_free events ("Feat: Context Parallel" 主要改动: events manage the K/V lifetime across
+ *   streams): before each refill and, after the ring, every slot the ring used.  The ring orders
+ *   every read of a slot before that fill, so results do not change; a read that escaped the
+ *   events would see NaN (the fill word 0x7FC07FC0 is NaN as two bf16 values and as an fp32).
+ *   When such a call's stream has drained, the slots in its workspace hold NaN.
+ * RA_DEBUG_ROCTX: the rank views mark the ring loop and each ring step with roctx ranges
+ *   ("ra fwd step 3 owner 12 (slot 0)", ...) for rocprofv3 --marker-trace; the roctx library is
+ *   opened on first use, and where it is absent the flag does nothing.
+ * RA_ERR_INVALID for a NULL context or unknown bits. */
+#define RA_DEBUG_POISON_SLOTS 1u
+#define RA_DEBUG_ROCTX 2u
+ra_status ra_set_debug(ra_context* ctx, uint32_t flags);
+
 /* ---- device entry points -------------------------------------------------------------- */
 
 /* Layout permutation ("Feat: Context Parallel" 主要改动; "上下文并行" "Zig-Zag Ring

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES) | set(L.OTHER)
@@ -113,6 +113,9 @@ def test_device_entry_points_reject_null_context_without_enqueueing():
     arr = L.pairs_array([(0, 0, 8, 8, L.RA_MASK_DIAG)])
     st = lib.ra_chunk_fwd(None, ctypes.byref(p), None, 8, None, None, 8, arr, 1, None, None, None, None)
     assert st == L.RA_ERR_INVALID
+    # the debug switch, too: no context, whatever the flags
+    assert lib.ra_set_debug(None, 0) == L.RA_ERR_INVALID
+    assert lib.ra_set_debug(None, L.RA_DEBUG_POISON_SLOTS | L.RA_DEBUG_ROCTX) == L.RA_ERR_INVALID
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
