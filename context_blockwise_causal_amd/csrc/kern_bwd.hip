@@ -392,6 +392,21 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
     }
     const int niter = (int)((q_end - q_begin + kKvBQ - 1) / kKvBQ);
     if (niter <= 0) continue;
+    // Steps that take the mask, as bounds on the step index t (scalar): all of them when some key
+    // of the wavefront lies past the tile; t < t_lo while a step reaches a key of the wavefront
+    // after its query (diagonal pair); t >= t_hi once a step reaches past the window / attention
+    // chunk of the wavefront's first key.
+    const bool wpart = kw + 32 > tr.nrows;
+    int t_lo = 0, t_hi = niter;
+    if (diag) {
+      const int64_t x = kwave + 31 - q_begin;  // steps with 32 t < x
+      t_lo = x <= 0 ? 0 : (int)((x + kKvBQ - 1) / kKvBQ);
+    }
+    if (has_hi) {
+      const int64_t y = wave_hi_min - (kKvBQ - 1) - q_begin;  // steps with 32 t > y
+      const int64_t th = y < 0 ? 0 : y / kKvBQ + 1;
+      t_hi = (int)(th < niter ? th : niter);
+    }
     const u16* Qp = reinterpret_cast<const u16*>(p.q) + (qhead + pr.q_row0) * D;
     const u16* dOp = reinterpret_cast<const u16*>(p.dO) + (qhead + pr.q_row0) * D;
     const float* lsep = p.lse + qhead + pr.q_row0;
@@ -549,8 +564,7 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
         }
         // excluded (key, query) pairs: keys past the range, keys after the query (diagonal pair),
         // queries past the window / attention chunk of the key
-        const bool edge = !kvalid || (diag && kwave + 31 > qbase) || (has_hi && qbase + kKvBQ - 1 > wave_hi_min);
-        if (edge) {
+        if (wpart || t < t_lo || t >= t_hi) {
           const int qmin = !kvalid ? 1 << 20 : (diag ? (int)(kwave - qbase) + lq : -1);
           const int qml = qmin - 8 * hh, qmh = hi32 - (int)qbase - 8 * hh;
 #pragma unroll
