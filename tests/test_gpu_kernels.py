@@ -286,6 +286,44 @@ def test_chunk_bwd_single_pair(ctx, D, Hq, Hkv, dtype, kind, entry):
         assert_close(to_f64(got), ref, dtype, name)
 
 
+@pytest.mark.parametrize("kind", ["FULL", "DIAG"])
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_short_loops_of_the_d128_kernels(ctx, n, kind):
+    """The D = 128 bf16 kernels run their main loops in ping-pong form, whose prologue and tail
+    differ for one, two and three iterations (tiles of 64 keys in the forward, steps of 32 query
+    rows in the dK/dV kernel): pairs of those lengths, ragged, forward and both backward entries."""
+    B, Hq, Hkv, D, dtype = 1, 4, 2, 128, "bf16"
+    kvlen = 64 * (n - 1) + 23  # forward: n key tiles
+    qlen = 32 * (n - 1) + 11   # backward: n query steps
+    if kind == "DIAG":  # one length: 1, 2, 3 key tiles and 1, 3, 5 query steps
+        kvlen = qlen = {1: 11, 2: 75, 3: 150}[n]
+    mask = {"FULL": L.RA_MASK_FULL, "DIAG": L.RA_MASK_DIAG}[kind]
+    qp, kp = O.pair_positions(O.FULL if kind == "FULL" else O.DIAG, qlen, kvlen)
+    prob = api.Problem(B, 2 * max(qlen, kvlen), Hq, Hkv, D, 1, "contiguous", dtype)
+    q = to_dev(rand_store((B, Hq, qlen, D), dtype, 81 + n), dtype)
+    k = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 91 + n), dtype)
+    v = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 101 + n), dtype)
+    do = to_dev(rand_store((B, Hq, qlen, D), dtype, 111 + n), dtype)
+    q64, k64, v64, do64 = (to_f64(t) for t in (q, k, v, do))
+    U, m, l = run_pairs_fwd(ctx, prob, q, k, v, [(0, 0, qlen, kvlen, mask)])
+    o, lse = api.ra_fwd_finalize(ctx, prob, U, m, l)
+    torch.cuda.synchronize()
+    ro, rl, rdelta = oracle_stats(q64, k64, v64, do64, qp, kp)
+    assert_close(to_f64(o), ro, dtype, f"O ({n} tiles)")
+    assert np.max(np.abs(to_f64(lse) - rl)) < 2e-3
+    lse_d = torch.tensor(rl, dtype=torch.float32, device="cuda")
+    dl_d = torch.tensor(rdelta, dtype=torch.float32, device="cuda")
+    rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, qp, kp)
+    for entry in ("recompute", "stored"):
+        dq = torch.zeros(B, Hq, qlen, D, device="cuda")
+        dk = torch.zeros(B, Hkv, kvlen, D, device="cuda")
+        dv = torch.zeros_like(dk)
+        chunk_bwd(entry, ctx, prob, q, do, lse_d, dl_d, k, v, [(0, 0, qlen, kvlen, mask)], dq, dk, dv)
+        torch.cuda.synchronize()
+        for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
+            assert_close(to_f64(got), ref, dtype, f"{name} ({entry}, {n} steps)")
+
+
 @pytest.mark.parametrize("entry", ["recompute", "stored"])
 @pytest.mark.parametrize("D,Hq,Hkv,dtype", CASES[:2])
 def test_chunk_bwd_zigzag_local_step_accumulates(ctx, D, Hq, Hkv, dtype, entry):
