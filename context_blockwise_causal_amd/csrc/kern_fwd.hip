@@ -241,6 +241,16 @@ __global__ __launch_bounds__(kNT, 2) void chunk_fwd_bf16_kernel(const KParams p)
 // wavefront issues MFMAs while the other does its softmax.  K/V tiles rotate through four LDS
 // buffers, loaded by the first team two tiles ahead with buffer loads to LDS (which, unlike the
 // global form, leave the compiler's waits for LDS reads exact).
+//
+// The loop is bound by instruction issue more than by any one unit, so its reads carry no address
+// arithmetic: the tile loop is unrolled over the four buffers, the four K tiles lie in the first
+// 64 KB of LDS and the four V tiles after them, and each operand read is a register formed once
+// per lane plus a compile-time offset (the buffer, the key step) in the instruction.
+
+template <int N>
+struct Step {
+  static constexpr int value = N;
+};
 
 constexpr int kPPRows = 256;  // query rows per workgroup (two teams of 128)
 constexpr int kPPNT = 512;    // threads per workgroup
@@ -248,8 +258,8 @@ constexpr int kPPNT = 512;    // threads per workgroup
 template <int D>
 __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p) {
   using C = FwdCfg<D>;
-  constexpr int BUF = 2 * C::TILE;  // K tile, then V tile
-  __shared__ __attribute__((aligned(16))) u16 lds[4 * BUF];
+  // K tile b at lds + b TILE, V tile b at lds + (4 + b) TILE
+  __shared__ __attribute__((aligned(16))) u16 lds[8 * C::TILE];
 
   const TileRef tr = map_tile(p, kPPRows);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -287,8 +297,27 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
       }
   }
 
-  const RowAddr ka0 = make_row_addr(perm32(lq), hh, D);
-  const TrAddr va = make_tr_addr(lane, D);
+  // Per-lane byte offsets of the operand reads, formed once: the K row operand of 16-deep step kk
+  // within a K tile (the row 32 further, with the same swizzle, is 64 D bytes on) and the two
+  // halves of the transposed V operand of d block db (key step c adds 32 c D bytes), the latter
+  // measured from the K tile of the same buffer index, 8 TILE bytes before its V tile, so that
+  // the buffer's offset stays within the reach of the instruction's immediate.
+  int kb[C::KK], vb[C::DB][2];
+  {
+    const RowAddr ka = make_row_addr(perm32(lq), hh, D);
+    const TrAddr va = make_tr_addr(lane, D);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      kb[kk] = (ka.base + ((16 * kk) ^ ka.g8)) * 2;
+      asm volatile("" : "+v"(kb[kk]));
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      vb[db][0] = (va.lo ^ (db << 5)) * 2 + 8 * C::TILE;
+      vb[db][1] = (va.hi ^ (db << 5)) * 2 + 8 * C::TILE;
+      asm volatile("" : "+v"(vb[db][0]), "+v"(vb[db][1]));
+    }
+  }
   const KRange& R = p.ranges[tr.range];
   for (int pi = 0; pi < R.npairs; ++pi) {
     const KPair pr = p.pairs[R.pair[pi]];
@@ -323,7 +352,7 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
 
     // The first team loads key tile kt (K then V, rows past the pair repeat its last row): 16
     // one-KB instructions per tile, 8 per wavefront.
-    auto load = [&](int64_t kt, u16* __restrict__ B) {
+    auto load = [&](int64_t kt, u16* __restrict__ Bk, u16* __restrict__ Bv) {
       const int64_t k0 = kt * kBN;
       const int last = (int)(pr.kv_len - k0 < kBN ? pr.kv_len - k0 : kBN) - 1;
       const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + k0 * D), 0, kBN * D * 2, kBufRsrcWord3);
@@ -334,8 +363,8 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
         const int i = k * 4 + w, row = i * RPI + lane / CH;
         const int c = (lane % CH) ^ swz(row, D);
         const unsigned off = (unsigned)((row < last ? row : last) * D + c * 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lvoid_t*)(B + i * 512), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lvoid_t*)(B + C::TILE + i * 512), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lvoid_t*)(Bk + i * 512), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lvoid_t*)(Bv + i * 512), 16, off, 0, 0, 0);
       }
     };
 
@@ -343,14 +372,15 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
     // into s[0]) after a vector phase.
     f32x16 s[2] = {f32x16{}, f32x16{}};
     // One phase for tile t (0-based within the pair's tiles from kt0): the matrix phase (mph: the
-    // P V contraction of tile t - 1 if pv, the scores of tile t if sc) or the vector phase.  Bc
-    // holds tile t, Bo tile t - 1, Bn receives tile t + 2 (first team, matrix phase).
-    auto phase = [&](bool mph, bool pv, bool sc, int t, u16* __restrict__ Bn, const u16* __restrict__ Bo,
-                     const u16* __restrict__ Bc) {
+    // P V contraction of tile t - 1 if pv, the scores of tile t if sc) or the vector phase.  Kc is
+    // the K tile of tile t, Vo the V tile of tile t - 1; Kn, Vn receive tile t + 2 (first team,
+    // matrix phase).
+    auto phase = [&](bool mph, bool pv, bool sc, int t, u16* __restrict__ Kn, u16* __restrict__ Vn,
+                     const u16* __restrict__ Vo, const u16* __restrict__ Kc) {
       const int64_t kbase = (kt0 + t) * kBN;
       if (mph) {
         __builtin_amdgcn_s_setprio(1);  // the matrix phase's MFMAs go ahead of the other wavefront's vector work
-        if (team == 0 && t + 2 < niter) load(kt0 + t + 2, Bn);
+        if (team == 0 && t + 2 < niter) load(kt0 + t + 2, Kn, Vn);
         if (pv) {
           // O^T += V^T P^T of tile t - 1: P^T for key step c is registers 8 (c & 1) .. of block c >> 1,
           // packed as bf16 into s[0]
@@ -362,14 +392,18 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
                                : c == 1 ? __builtin_shufflevector(s[0], s[0], 4, 5, 6, 7)
                                         : c == 2 ? __builtin_shufflevector(s[0], s[0], 8, 9, 10, 11)
                                                  : __builtin_shufflevector(s[0], s[0], 12, 13, 14, 15));
-          TrAddr tv = va;  // the per-db addresses are formed here, not kept live across the loop
-          asm volatile("" : "+v"(tv.lo), "+v"(tv.hi));
           __builtin_amdgcn_sched_barrier(0);
           // the 16 MFMAs in the order (c, db) (consecutive ones into different accumulators), the A
           // operand V^T(c, db) read kWin - 1 MFMAs ahead
           constexpr int kWin = 8;
           bf16x8 A[kWin];
-          auto load_op = [&](int i) { A[i % kWin] = tr_operand(Bo + C::TILE, tv, D, i / C::DB, i % C::DB); };
+          auto load_op = [&](int i) {
+            const int c = i / C::DB, db = i % C::DB;
+            const char* const t0 = reinterpret_cast<const char*>(Vo) - 8 * C::TILE + 32 * c * D;
+            const v4i16 lo = ds_read_tr16(reinterpret_cast<const u16*>(t0 + vb[db][0]));
+            const v4i16 hi = ds_read_tr16(reinterpret_cast<const u16*>(t0 + vb[db][1]));
+            A[i % kWin] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
 #pragma unroll
           for (int i = 0; i < kWin - 1; ++i) load_op(i);
 #pragma unroll
@@ -383,14 +417,11 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
         __builtin_amdgcn_sched_barrier(0);
         if (sc) {
           // S^T = K Q^T of tile t for its two 32-key blocks; K rows read two kk ahead
-          // (rows r and r + 32 share their swizzle: the second row is an immediate offset away)
-          RowAddr r0 = ka0;
-          asm volatile("" : "+v"(r0.base), "+v"(r0.g8));
           bf16x8 k0o[3], k1o[3];
           auto load_k = [&](int kk) {
-            const u16* const a = Bc + r0.base + ((16 * kk) ^ r0.g8);
+            const char* const a = reinterpret_cast<const char*>(Kc) + kb[kk];
             k0o[kk % 3] = *reinterpret_cast<const bf16x8*>(a);
-            k1o[kk % 3] = *reinterpret_cast<const bf16x8*>(a + 32 * D);
+            k1o[kk % 3] = *reinterpret_cast<const bf16x8*>(a + 64 * D);
           };
           load_k(0);
           load_k(1);
@@ -471,28 +502,37 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_fwd_pp_kernel(const KParams p)
                       w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
       }
     };
-    auto run = [&](bool mph, bool pv, bool sc, int t) {
-      u16* const tiles = lds;
-      u16* const Bc = tiles + (t & 3) * BUF;
-      u16* const Bn = tiles + ((t + 2) & 3) * BUF;
-      u16* const Bo = tiles + ((t + 3) & 3) * BUF;
-      phase(mph, pv, sc, t, Bn, Bo, Bc);
+    // A phase of tile t, whose buffer index t & 3 is the compile-time P.
+    auto run = [&](auto P, bool mph, bool pv, bool sc, int t) {
+      constexpr int b = decltype(P)::value;
+      phase(mph, pv, sc, t, lds + ((b + 2) & 3) * C::TILE, lds + (4 + ((b + 2) & 3)) * C::TILE,
+            lds + (4 + ((b + 3) & 3)) * C::TILE, lds + b * C::TILE);
       phase_barrier();
     };
 
     if (team == 0) {
-      load(kt0, lds);
-      if (niter > 1) load(kt0 + 1, lds + BUF);
+      load(kt0, lds, lds + 4 * C::TILE);
+      if (niter > 1) load(kt0 + 1, lds + C::TILE, lds + 5 * C::TILE);
     }
     wait_vmem();
     __syncthreads();
     // Each loop step is the vector phase of tile t and the matrix phase of tile t + 1 (the first M
     // has no P V, the last no scores).  The second team runs one phase behind the first.
-    if (team == 1) phase_barrier();
-    for (int t = -1; t < niter; ++t) {
-      if (t >= 0) run(false, false, false, t);
+    // (the vector phase reads no tile: its buffer index is immaterial)
+    auto step = [&](auto P, int t) {  // P: the buffer of tile t + 1
+      if (t >= 0) run(P, false, false, false, t);
       else phase_barrier();
-      run(true, t >= 0, t + 1 < niter, t + 1);
+      run(P, true, t >= 0, t + 1 < niter, t + 1);
+    };
+    if (team == 1) phase_barrier();
+    for (int t = -1; t < niter; t += 4) {
+      step(Step<0>{}, t);
+      if (t + 1 >= niter) break;
+      step(Step<1>{}, t + 1);
+      if (t + 2 >= niter) break;
+      step(Step<2>{}, t + 2);
+      if (t + 3 >= niter) break;
+      step(Step<3>{}, t + 3);
     }
     if (team == 0) phase_barrier();
   }
