@@ -343,13 +343,15 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
   u16* const tiles = lds + kPPKeys * VP;
   u16* const stg = tiles + 4 * BUF;
 
-  const TileRef tr = map_tile(p, kPPKeys);
+  // q_per_wg query heads of one key/value group in turn: one prologue (K, V) and one epilogue (the
+  // dK/dV atomics) for all of them
+  const int qgroup = p.q_per_wg > 1 ? p.q_per_wg : 1;
+  const TileRef tr = map_tile(p, kPPKeys, qgroup);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int team = w >> 2, kw = 32 * w;  // kw: the wavefront's first key within the tile
   const int kl = kw + lq;                // this lane's key within the tile
   const bool kvalid = kl < tr.nrows, wvalid = kw < tr.nrows;
   const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
-  const int64_t qhead = ((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows;
   const int64_t dkvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.dkv_head_rows;
   const u16* __restrict__ Kg = reinterpret_cast<const u16*>(p.k) + (kvhead + tr.row0) * D;
   const u16* __restrict__ Vg = reinterpret_cast<const u16*>(p.v) + (kvhead + tr.row0) * D;
@@ -373,6 +375,9 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
   const float l2s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_amdgcn_logf(p.scale))));
 
   const KRange& R = p.ranges[tr.range];
+  for (int gi = 0; gi < qgroup; ++gi) {
+  const int hq = tr.hq + gi;
+  const int64_t qhead = ((int64_t)tr.b * p.Hq + hq) * p.q_head_rows;
   for (int pi = 0; pi < R.npairs; ++pi) {
     const KPair pr = p.pairs[R.pair[pi]];
     const bool diag = pr.mask == RA_MASK_DIAG;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
     // stored scale * dS^T: the block row of the wavefront's 32 keys (see ds_block_off); only rows
     // of wavefronts holding a valid key are stored (they lie inside the pair's 128-row granules)
     char* const dsw = DS ? reinterpret_cast<char*>(reinterpret_cast<u16*>(p.ds) + pr.ds_off +
-                                                   (((int64_t)tr.b * p.Hq + tr.hq) * pr.ds_rows + kwave) * pr.ds_ld)
+                                                   (((int64_t)tr.b * p.Hq + hq) * pr.ds_rows + kwave) * pr.ds_ld)
                          : nullptr;
 
     // Carried from one phase to the next: S and dP after a matrix phase; P and scale * dS (bf16,
@@ -650,6 +655,8 @@ __global__ __launch_bounds__(kPPNT, 2) void chunk_bwd_kv_pp_kernel(const KParams
     }
     if (team == 0) phase_barrier();
   }
+
+  }  // query heads of the group
 
   // Epilogue: the teams in turn; each wavefront stages its 32 x D block in LDS and adds it to dk /
   // dv row by row with fp32 atomics (the query heads of a key/value head add into the same rows).
@@ -1029,15 +1036,26 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
   }
 }
 
+// Query heads per ping-pong dK/dV workgroup (one workgroup per CU): two heads of a key/value group
+// share one workgroup's K/V prologue and dK/dV atomics.  Above 256 workgroups that takes no more
+// rounds of workgroups than one head each (ceil(n / 512) twice-longer rounds against ceil(n / 256))
+// and halves those fixed costs; at 256 or fewer it would double the length of the one round.
+int kv_group(const KParams& kv, int64_t nkv) {
+  return (kv.n_rep % 2 == 0 && nkv > 256) ? 2 : 1;
+}
+
 template <int D>
 int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   int e;
   const int64_t nkv = kv.dk ? (int64_t)kv.B * kv.Hq * kv.tiles_per_head : 0;
   const int64_t nq = q.U ? (int64_t)q.B * q.Hq * q.tiles_per_head : 0;
   if (nkv > 0) {
-    if (D == 128)
-      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, true>), dim3((unsigned)nkv), dim3(kPPNT), 0, (hipStream_t)stream, kv);
-    else
+    if (D == 128) {
+      KParams g = kv;
+      g.q_per_wg = kv_group(kv, nkv);
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, true>), dim3((unsigned)(nkv / g.q_per_wg)), dim3(kPPNT), 0,
+                         (hipStream_t)stream, g);
+    } else
       hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, true>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }
@@ -1073,9 +1091,12 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
     qs = (hipStream_t)fork->side;
   }
   if (do_kv) {
-    if (D == 128)
-      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, false>), dim3((unsigned)nkv), dim3(kPPNT), 0, (hipStream_t)stream, kv);
-    else
+    if (D == 128) {
+      KParams g = kv;
+      g.q_per_wg = kv_group(kv, nkv);
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, false>), dim3((unsigned)(nkv / g.q_per_wg)), dim3(kPPNT), 0,
+                         (hipStream_t)stream, g);
+    } else
       hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, false>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
   }

@@ -226,11 +226,14 @@ struct TileRef {
 // heavy tiles would work far longer than the one holding its light tiles: the logical order is
 // then dealt out round-robin (logical index = hardware index), which gives every XCD every
 // eighth tile of each head.
-__device__ __forceinline__ TileRef map_tile(const KParams& p, int64_t tile_rows) {
+// With group > 1 a workgroup takes `group` consecutive query heads (which share a key/value
+// head): the heads counted here are the groups, and r.hq is the group's first query head.
+__device__ __forceinline__ TileRef map_tile(const KParams& p, int64_t tile_rows, int group = 1) {
   const int64_t nblk = (int64_t)gridDim.x;
   const int64_t bid = (int64_t)blockIdx.x;
+  const int heads = p.Hq / group;
   int64_t logical = bid;
-  if ((((int64_t)p.B * p.Hq) & 7) == 0) {
+  if ((((int64_t)p.B * heads) & 7) == 0) {
     const int64_t x = bid & 7, k = bid >> 3;
     const int64_t q = nblk >> 3, rem = nblk & 7;
     logical = x * q + (x < rem ? x : rem) + k;
@@ -238,8 +241,8 @@ __device__ __forceinline__ TileRef map_tile(const KParams& p, int64_t tile_rows)
   const int64_t head = logical / p.tiles_per_head;
   int64_t t = logical - head * p.tiles_per_head;
   TileRef r;
-  r.b = (int)(head / p.Hq);
-  r.hq = (int)(head - (int64_t)r.b * p.Hq);
+  r.b = (int)(head / heads);
+  r.hq = (int)(head - (int64_t)r.b * heads) * group;
   r.g = r.hq / p.n_rep;
   int ri = 0;
 #pragma unroll

@@ -98,6 +98,7 @@ struct KParams {
   int64_t window;         // sliding window (0 = none)
   int64_t attn_chunk;     // attention chunk (0 = none)
   int32_t fresh;          // forward: start every row from the empty state instead of loading U, m, l
+  int32_t q_per_wg;       // dK/dV kernel (D = 128): query heads of one key/value group per workgroup (0 or 1: one)
   int32_t nranges;
   int64_t tiles_per_head;
   KRange ranges[4];

@@ -286,6 +286,38 @@ def test_chunk_bwd_single_pair(ctx, D, Hq, Hkv, dtype, kind, entry):
         assert_close(to_f64(got), ref, dtype, name)
 
 
+@pytest.mark.parametrize("Hkv", [32, 16])
+@pytest.mark.parametrize("kind", ["FULL", "DIAG"])
+def test_chunk_bwd_two_query_heads_per_workgroup(ctx, kind, Hkv):
+    """With more than 256 dK/dV workgroups and an even number of query heads per key/value head,
+    each D = 128 workgroup takes two query heads of its group in turn (one K/V prologue, one
+    set of dK/dV atomics): 64 query heads, groups of 2 and 4, 5 key tiles of 256 (the last ragged),
+    both entries, every element against the oracle."""
+    B, Hq, D, dtype = 1, 64, 128, "bf16"
+    kvlen = 1100
+    qlen = 100 if kind == "FULL" else kvlen
+    mask = {"FULL": L.RA_MASK_FULL, "DIAG": L.RA_MASK_DIAG}[kind]
+    prob = api.Problem(B, 2 * kvlen, Hq, Hkv, D, 1, "contiguous", dtype)
+    q = to_dev(rand_store((B, Hq, qlen, D), dtype, 121), dtype)
+    k = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 122), dtype)
+    v = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 123), dtype)
+    do = to_dev(rand_store((B, Hq, qlen, D), dtype, 124), dtype)
+    qp, kp = O.pair_positions(O.FULL if kind == "FULL" else O.DIAG, qlen, kvlen)
+    q64, k64, v64, do64 = (to_f64(t) for t in (q, k, v, do))
+    _, lse, delta = oracle_stats(q64, k64, v64, do64, qp, kp)
+    lse_d = torch.tensor(lse, dtype=torch.float32, device="cuda")
+    dl_d = torch.tensor(delta, dtype=torch.float32, device="cuda")
+    rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, qp, kp)
+    for entry in ("recompute", "stored"):
+        dq = torch.zeros(B, Hq, qlen, D, device="cuda")
+        dk = torch.zeros(B, Hkv, kvlen, D, device="cuda")
+        dv = torch.zeros_like(dk)
+        chunk_bwd(entry, ctx, prob, q, do, lse_d, dl_d, k, v, [(0, 0, qlen, kvlen, mask)], dq, dk, dv)
+        torch.cuda.synchronize()
+        for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
+            assert_close(to_f64(got), ref, dtype, f"{name} ({entry})")
+
+
 @pytest.mark.parametrize("kind", ["FULL", "DIAG"])
 @pytest.mark.parametrize("n", [1, 2, 3])
 def test_short_loops_of_the_d128_kernels(ctx, n, kind):
