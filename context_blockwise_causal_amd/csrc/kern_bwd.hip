@@ -1036,14 +1036,6 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
   }
 }
 
-// Query heads per ping-pong dK/dV workgroup (one workgroup per CU): two heads of a key/value group
-// share one workgroup's K/V prologue and dK/dV atomics.  Above 256 workgroups that takes no more
-// rounds of workgroups than one head each (ceil(n / 512) twice-longer rounds against ceil(n / 256))
-// and halves those fixed costs; at 256 or fewer it would double the length of the one round.
-int kv_group(const KParams& kv, int64_t nkv) {
-  return (kv.n_rep % 2 == 0 && nkv > 256) ? 2 : 1;
-}
-
 template <int D>
 int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFork* fork) {
   int e;
@@ -1051,10 +1043,9 @@ int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFo
   const int64_t nq = q.U ? (int64_t)q.B * q.Hq * q.tiles_per_head : 0;
   if (nkv > 0) {
     if (D == 128) {
-      KParams g = kv;
-      g.q_per_wg = kv_group(kv, nkv);
-      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, true>), dim3((unsigned)(nkv / g.q_per_wg)), dim3(kPPNT), 0,
-                         (hipStream_t)stream, g);
+      const int64_t G = kv.q_per_wg > 1 ? kv.q_per_wg : 1;
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, true>), dim3((unsigned)(nkv / G)), dim3(kPPNT), 0,
+                         (hipStream_t)stream, kv);
     } else
       hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, true>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;
@@ -1092,10 +1083,9 @@ int launch_bwd(const KParams& kv, const KParams& q, void* stream, const BwdFork*
   }
   if (do_kv) {
     if (D == 128) {
-      KParams g = kv;
-      g.q_per_wg = kv_group(kv, nkv);
-      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, false>), dim3((unsigned)(nkv / g.q_per_wg)), dim3(kPPNT), 0,
-                         (hipStream_t)stream, g);
+      const int64_t G = kv.q_per_wg > 1 ? kv.q_per_wg : 1;
+      hipLaunchKernelGGL((chunk_bwd_kv_pp_kernel<D, false>), dim3((unsigned)(nkv / G)), dim3(kPPNT), 0,
+                         (hipStream_t)stream, kv);
     } else
       hipLaunchKernelGGL((chunk_bwd_kv_kernel<D, false>), dim3((unsigned)nkv), dim3(kNT), 0, (hipStream_t)stream, kv);
     if ((e = (int)hipGetLastError())) return e;

@@ -168,6 +168,7 @@ int run_bwd(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, void* 
   if (s.dtype == RA_BF16) {
     KParams kq = kp;
     build_ranges(&kp, pairs, n, false, s.D == 128 ? kBwdPPTileRows : kBwdTileRows);
+    kp.q_per_wg = kv_heads_per_wg(kp);
     build_ranges(&kq, pairs, n, true, kBwdQTileRows);
     return kp.nranges ? launch_chunk_bwd_bf16(kp, kq, stream, fork) : 0;
   }
@@ -180,6 +181,7 @@ int run_bwd_ds(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, voi
                const BwdFork* fork) {
   KParams kq = kp;
   build_ranges(&kp, pairs, n, false, s.D == 128 ? kBwdPPTileRows : kBwdTileRows);
+  kp.q_per_wg = kv_heads_per_wg(kp);
   build_ranges(&kq, pairs, n, true, kBwdDsTileRows);
   ds_layout(s, pairs, n, &kp);
   ds_layout(s, pairs, n, &kq);

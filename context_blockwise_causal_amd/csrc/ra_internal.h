@@ -105,6 +105,16 @@ struct KParams {
   KPair pairs[4];
 };
 
+// Query heads per workgroup of the D = 128 dK/dV kernel (call after build_ranges): two heads of a
+// key/value group share one workgroup's K/V prologue and dK/dV atomics when the launch has more
+// than 256 workgroups (one per CU) -- never more rounds of workgroups (ceil(n / 512) twice-longer
+// rounds against ceil(n / 256)), half the fixed costs; at 256 or fewer it would lengthen the one
+// round.
+inline int32_t kv_heads_per_wg(const KParams& kp) {
+  const int64_t n = (int64_t)kp.B * kp.Hq * kp.tiles_per_head;
+  return (kp.D == 128 && kp.n_rep % 2 == 0 && n > 256) ? 2 : 1;
+}
+
 // Builds the range table: groups non-SKIP pairs by their outer range and assigns tiles of
 // `tile_rows` rows.  by_q selects the forward grouping (Q ranges) or the backward (K/V).
 void build_ranges(KParams* kp, const ra_pair* pairs, int32_t n, bool by_q, int64_t tile_rows);

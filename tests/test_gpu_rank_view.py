@@ -73,6 +73,13 @@ CASES = [
     # times, the second running state and second dK/dV stream
     (1, 64, 4, 2, 128, 16, "zigzag", "bf16"),
     (1, 64, 4, 2, 128, 16, "contiguous", "bf16"),
+    # one query head per key/value head at D = 128: every dK/dV workgroup holds the whole sum of
+    # its rows, so the kernel writes the owner's bf16 rows itself (no accumulator, no cast)
+    (1, 256, 4, 4, 128, 4, "zigzag", "bf16"),
+    (1, 200, 2, 2, 128, 2, "contiguous", "bf16"),
+    # 128 query heads in groups of 2: the local step has more than 256 dK/dV workgroups (two heads
+    # each, rows written directly), the other step fewer (one head each, atomics and the cast)
+    (1, 768, 128, 64, 128, 2, "zigzag", "bf16"),
 ]
 
 
