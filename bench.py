@@ -308,7 +308,7 @@ def main():
                         wl.batch * wl.heads_kv * (wl.seq_len // wl.cp) * wl.head_dim * esize)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs a single rank view at a time on one "
+        print("bench.py measures one GPU only: the library runs a single rank view at a time on one "
               "MI355X (the ring is simulated on one device); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -34,7 +34,7 @@ What it computes, and from which passage of the pages:
   recompute backward the "Feat: Context Parallel" p2p mode describes (probabilities recomputed
   from the saved log-sum-exp; K/V gradients returned to the owner).
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
   scale = 1/sqrt(head_dim); the softmax sum runs over the row's visible keys; masked scores are
   excluded exactly (probability 0); LSE is the natural log; a rank view's dK/dV is the
   contribution of that rank's query rows only.
