@@ -90,9 +90,10 @@ const Roctx& roctx() {
       if (!h) continue;
       r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
       r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
-      if (r.push && r.pop) return;
+      if (r.push && r.pop) return;  // kept open for the life of the process
       r.push = nullptr;
       r.pop = nullptr;
+      dlclose(h);
     }
   });
   return r;
