@@ -884,56 +884,72 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_q_kernel(const KParams p) {
 // zero the excluded entries of the operand before the MFMA; interior tiles are fully visible and
 // were written.
 
-constexpr int kDsBM = 128;  // query rows per workgroup (columns of a dS^T tile)
-constexpr int kDsBN = 64;   // keys per tile (rows of a dS^T tile)
+// A workgroup of the dQ kernel takes QB query blocks of 32 per wavefront (128 QB queries) and
+// steps over 64 / QB keys at a time, so that every step is 16 MFMAs per wavefront either way; with
+// QB = 2 each K^T operand read from LDS feeds two MFMAs.
+template <int QB> constexpr int ds_bm() { return 128 * QB; }  // query rows per workgroup
+template <int QB> constexpr int ds_bn() { return 64 / QB; }   // keys per tile
 
-// A workgroup's 64-key x 128-query dS^T tile in LDS: its 16 half-blocks (32 keys x 16 queries,
-// 1 KB: key block kb, query block qs = the wavefront that reads it, half c) at half-block
-// h = (4 kb + qs) * 2 + c, each in the global layout (key k, query 8 hh + e at 16 k + 8 hh + e) and
-// padded to 1152 bytes, so that the two query halves a transposed read takes at once sit 32 banks
-// apart.
+// A workgroup's dS^T tile in LDS: its 16 half-blocks (32 keys x 16 queries, 1 KB: key block kb,
+// query block qs of the workgroup, half c; wavefront w reads query blocks QB w .. QB w + QB - 1)
+// at half-block h = (4 QB kb + qs) * 2 + c, each in the global layout (key k, query 8 hh + e at
+// 16 k + 8 hh + e) and padded to 1152 bytes, so that the two query halves a transposed read takes
+// at once sit 32 banks apart.
 constexpr int kDsHalf = 576;  // elements per padded half-block
 
 // Issues the direct loads of one dS^T tile (keys key0 .., queries q0 .. of the slab S of one
-// (batch, head)): each instruction copies one contiguous 1 KB half-block, lane i its 16-byte chunk
-// i.  Keys past the pair (up to the slab's 128-row granule) hold values the masks exclude.
-__device__ __forceinline__ void issue_ds_tile(const u16* __restrict__ S, int64_t ld, int64_t key0, int64_t q0,
-                                              u16* tile) {
+// (batch, head), leading dimension ld; key0 and q0 multiples of 32): each instruction copies one
+// contiguous 1 KB half-block, lane i its 16-byte chunk i, past the caches (read once).  The buffer
+// resource spans the tile's key-block rows, so with QB = 2 query blocks past the slab's width (the
+// last tile of a pair can reach past its 128-column granule) read as out of range rather than
+// another row's data; they feed only query columns past the pair, which are never stored.  Keys
+// past the pair (up to the slab's 128-row granule) hold values the masks exclude.
+template <int QB>
+__device__ __forceinline__ void issue_ds_tile(const u16* S, int64_t ld, int64_t key0, int64_t q0, u16* tile) {
   const int lane = threadIdx.x & 63, w = wave_id();
-  const u16* const blk = S + (key0 >> 5) * 32 * ld + (q0 >> 5) * 1024 + 8 * lane;
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(S + (key0 >> 5) * 32 * ld), 0,
+                                                     (int)(ds_bn<QB>() * ld * 2), kBufRsrcWord3);
+  const unsigned base = (unsigned)((q0 >> 5) * 1024 * 2) + 16u * lane;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int h = 4 * w + k, kb = h >> 3, qs = (h >> 1) & 3, c = h & 1;
-    g2lds16_nt(blk + kb * 32 * ld + qs * 1024 + c * 512, tile + h * kDsHalf);
+    const int h = 4 * k + w, c = h & 1, q = h >> 1, kb = q / (4 * QB), qs = q % (4 * QB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lvoid_t*)(tile + h * kDsHalf), 16,
+        base + (unsigned)(kb * 32 * ld * 2) + (unsigned)(qs * 2048 + c * 1024), 0, 0, 2);
   }
 }
 
-template <int D>
+template <int D, int QB>
 __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p) {
   constexpr int DB = D / 32;
-  constexpr int KT = kDsBN * D;       // elements of one K tile
-  constexpr int ST = 16 * kDsHalf;    // elements of one dS^T tile (64 keys x 128 queries, padded)
+  constexpr int BM = ds_bm<QB>(), BN = ds_bn<QB>();
+  constexpr int KS = BN / 16;         // 16-key MFMA steps per tile
+  constexpr int KT = BN * D;          // elements of one K tile
+  constexpr int ST = 16 * kDsHalf;    // elements of one dS^T tile (BN keys x BM queries, padded)
   // two buffers of (K tile, dS^T tile), read and filled through __restrict__ pointers
   __shared__ __attribute__((aligned(16))) u16 buf[2 * (KT + ST)];
 
-  const TileRef tr = map_tile(p, kDsBM);
+  const TileRef tr = map_tile(p, BM);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, lq = lane & 31, hh = lane >> 5;
-  const int qi = 32 * w + lq;
-  const bool qvalid = qi < tr.nrows;
-  const int64_t qrow = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi;
+  // the lane's query in each of the wavefront's query blocks: qi0 + 32 j
+  const int qi0 = 32 * QB * w + lq;
+  const int64_t qrow0 = (((int64_t)tr.b * p.Hq + tr.hq) * p.q_head_rows) + tr.row0 + qi0;
   const int64_t kvhead = ((int64_t)tr.b * p.Hkv + tr.g) * p.kv_head_rows;
   const int64_t head = (int64_t)tr.b * p.Hq + tr.hq;
 
-  f32x16 dq[DB];
+  // dQ^T accumulators: dq[j][db] holds query block j's dQ^T rows 32 db .. 32 db + 31
+  f32x16 dq[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[j][db] = f32x16{};
 
   const TrAddr kt = make_tr_addr(lane, D);      // K^T out of the [key][d] tile
   // dS^T columns out of the half-blocks: lane j of 16-lane group g addresses key 8 (g >> 1) + j / 4
   // (+4 for the second read, +16 per odd key step, + one key block per two steps) and queries
-  // 16 (g & 1) + 4 (j % 4) .. +3 of this wavefront's query block
+  // 16 (g & 1) + 4 (j % 4) .. +3 of its query block
   const int dsg = lane >> 4, dsj = lane & 15;
-  const int dsaddr = ((4 * 0 + w) * 2 + (dsg & 1)) * kDsHalf + (8 * (dsg >> 1) + (dsj >> 2)) * 16 +
+  const int dsaddr = (2 * QB * w + (dsg & 1)) * kDsHalf + (8 * (dsg >> 1) + (dsj >> 2)) * 16 +
                      ((dsj & 3) >> 1) * 8 + (dsj & 1) * 4;
   const u16* Kg = reinterpret_cast<const u16*>(p.k);
   const KRange& R = p.ranges[tr.range];
@@ -941,78 +957,91 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
     const KPair pr = p.pairs[R.pair[pi]];
     const bool diag = pr.mask == RA_MASK_DIAG;
     const int64_t qloc0 = tr.row0 - pr.q_row0;
-    const int64_t iq = qloc0 + qi;
     int64_t key_end = pr.kv_len;
     if (diag && qloc0 + tr.nrows < key_end) key_end = qloc0 + tr.nrows;
-    const int nkt = (int)((key_end + kDsBN - 1) / kDsBN);
+    const int nkt = (int)((key_end + BN - 1) / BN);
     const u16* Kp = Kg + (kvhead + pr.kv_row0) * D;
-    // the pair's dS^T slab of this (batch, head); this workgroup reads its 128 query columns
+    // the pair's dS^T slab of this (batch, head); this workgroup reads its BM query columns
     const u16* Sp = reinterpret_cast<const u16*>(p.ds) + pr.ds_off + head * pr.ds_rows * pr.ds_ld;
-    const int64_t wq_first = qloc0 + 32 * w;
-    const bool wave_has_rows = 32 * w < tr.nrows;
+    const int64_t wq_first = qloc0 + 32 * QB * w;   // the wavefront's first query (pair-local)
+    const bool wave_has_rows = 32 * QB * w < tr.nrows;
     const bool has_lo = p.window > 0 || p.attn_chunk > 0;
-    int64_t lo = 0, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
+    int64_t lo[QB] = {}, wave_lo = 0, wave_lo_max = 0, kt0 = 0;
     if (has_lo) {
-      lo = lowest_key(pr.q_pos0 + iq, p.window, p.attn_chunk) - pr.kv_pos0;
+#pragma unroll
+      for (int j = 0; j < QB; ++j)
+        lo[j] = lowest_key(pr.q_pos0 + qloc0 + qi0 + 32 * j, p.window, p.attn_chunk) - pr.kv_pos0;
       wave_lo = lowest_key(pr.q_pos0 + wq_first, p.window, p.attn_chunk) - pr.kv_pos0;
-      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 31, p.window, p.attn_chunk) - pr.kv_pos0;
+      wave_lo_max = lowest_key(pr.q_pos0 + wq_first + 32 * QB - 1, p.window, p.attn_chunk) - pr.kv_pos0;
       const int64_t tile_lo = lowest_key(pr.q_pos0 + qloc0, p.window, p.attn_chunk) - pr.kv_pos0;
-      kt0 = tile_lo > 0 ? tile_lo / kDsBN : 0;
+      kt0 = tile_lo > 0 ? tile_lo / BN : 0;
     }
 
     auto step = [&](const u16* __restrict__ kb, const u16* __restrict__ sb, u16* __restrict__ nk,
                     u16* __restrict__ ns, int t) {
-      const int64_t kbase = (int64_t)t * kDsBN;
+      const int64_t kbase = (int64_t)t * BN;
       if (t + 1 < nkt) {
-        issue_tile<D, kDsBN, 4>(Kp + (kbase + kDsBN) * D, pr.kv_len - kbase - kDsBN, nk);
-        issue_ds_tile(Sp, pr.ds_ld, kbase + kDsBN, qloc0, ns);
+        issue_tile<D, BN, 4>(Kp + (kbase + BN) * D, pr.kv_len - kbase - BN, nk);
+        issue_ds_tile<QB>(Sp, pr.ds_ld, kbase + BN, qloc0, ns);
       }
-      const bool active = wave_has_rows && !(diag && kbase > wq_first + 31) &&
-                          !(has_lo && kbase + kDsBN - 1 < wave_lo);
+      const bool active = wave_has_rows && !(diag && kbase > wq_first + 32 * QB - 1) &&
+                          !(has_lo && kbase + BN - 1 < wave_lo);
       if (active) {
-        // B operand dS^T for key step c: lane holds dS^T[16c + 8hh + e][its query], e = 0..7
-        bf16x8 dsb[4];
+        // B operands dS^T for query block j and key step c: lane holds
+        // dS^T[16c + 8hh + e][its query of block j], e = 0..7
+        bf16x8 dsb[QB][KS];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int off = dsaddr + (c >> 1) * 8 * kDsHalf + (c & 1) * 256;
-          const v4i16 lo = ds_read_tr16(sb + off), hi = ds_read_tr16(sb + off + 64);
-          dsb[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-        const bool edge = (kbase + kDsBN > pr.kv_len) || (diag && kbase + kDsBN - 1 > wq_first) ||
+        for (int j = 0; j < QB; ++j)
+#pragma unroll
+          for (int c = 0; c < KS; ++c) {
+            const int off = dsaddr + ((c >> 1) * 8 * QB + 2 * j) * kDsHalf + (c & 1) * 256;
+            const v4i16 lo4 = ds_read_tr16(sb + off), hi4 = ds_read_tr16(sb + off + 64);
+            dsb[j][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        const bool edge = (kbase + BN > pr.kv_len) || (diag && kbase + BN - 1 > wq_first) ||
                           (has_lo && kbase < wave_lo_max);
         if (edge) {
-          // visible keys of this lane's query, as tile offsets [kmin, kmax]
-          const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
-          const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > kDsBN - 1 ? kDsBN - 1 : lim - kbase));
-          const int kmin = has_lo ? (int)(lo - kbase < 0 ? 0 : (lo - kbase > kDsBN ? kDsBN : lo - kbase)) : 0;
-          // element e of step c is key 16 c + 8 hh + e: compare the compile-time part against the
-          // bounds shifted by 8 hh; bf16 element 2 i + b is half b of 32-bit word i
-          const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            u32x4 wv = __builtin_bit_cast(u32x4, dsb[c]);
+          for (int j = 0; j < QB; ++j) {
+            // visible keys of this lane's query in block j, as tile offsets [kmin, kmax]
+            const int64_t iq = qloc0 + qi0 + 32 * j;
+            const int64_t lim = diag ? (iq < pr.kv_len - 1 ? iq : pr.kv_len - 1) : pr.kv_len - 1;
+            const int kmax = (int)(lim - kbase < -1 ? -1 : (lim - kbase > BN - 1 ? BN - 1 : lim - kbase));
+            const int kmin = has_lo ? (int)(lo[j] - kbase < 0 ? 0 : (lo[j] - kbase > BN ? BN : lo[j] - kbase)) : 0;
+            // element e of step c is key 16 c + 8 hh + e: compare the compile-time part against
+            // the bounds shifted by 8 hh; bf16 element 2 i + b is half b of 32-bit word i
+            const int kmh = kmax - 8 * hh, kml = kmin - 8 * hh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int k0 = 16 * c + 2 * i;
-              const unsigned lo16 = (k0 >= kml && k0 <= kmh) ? 0xFFFFu : 0u;
-              const unsigned hi16 = (k0 + 1 >= kml && k0 + 1 <= kmh) ? 0xFFFF0000u : 0u;
-              wv[i] &= lo16 | hi16;
+            for (int c = 0; c < KS; ++c) {
+              u32x4 wv = __builtin_bit_cast(u32x4, dsb[j][c]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int k0 = 16 * c + 2 * i;
+                const unsigned lo16 = (k0 >= kml && k0 <= kmh) ? 0xFFFFu : 0u;
+                const unsigned hi16 = (k0 + 1 >= kml && k0 + 1 <= kmh) ? 0xFFFF0000u : 0u;
+                wv[i] &= lo16 | hi16;
+              }
+              dsb[j][c] = __builtin_bit_cast(bf16x8, wv);
             }
-            dsb[c] = __builtin_bit_cast(bf16x8, wv);
           }
         }
+        // each K^T operand feeds the wavefront's QB query blocks
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) dq[db] = mfma32(tr_operand(kb, kt, D, c, db), dsb[c], dq[db]);
+          for (int c = 0; c < KS; ++c) {
+            const bf16x8 a = tr_operand(kb, kt, D, c, db);
+#pragma unroll
+            for (int j = 0; j < QB; ++j) dq[j][db] = mfma32(a, dsb[j][c], dq[j][db]);
+          }
       }
       wait_vmem();
       __syncthreads();
     };
 
     if (kt0 >= nkt) continue;  // uniform over the workgroup
-    issue_tile<D, kDsBN, 4>(Kp + kt0 * kDsBN * D, pr.kv_len - kt0 * kDsBN, buf);
-    issue_ds_tile(Sp, pr.ds_ld, kt0 * kDsBN, qloc0, buf + KT);
+    issue_tile<D, BN, 4>(Kp + kt0 * BN * D, pr.kv_len - kt0 * BN, buf);
+    issue_ds_tile<QB>(Sp, pr.ds_ld, kt0 * BN, qloc0, buf + KT);
     wait_vmem();
     __syncthreads();
     for (int t = (int)kt0; t < nkt; ++t) {
@@ -1022,7 +1051,10 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
     }
   }
 
-  if (qvalid) {
+#pragma unroll
+  for (int jq = 0; jq < QB; ++jq) {
+    if (qi0 + 32 * jq >= tr.nrows) continue;
+    const int64_t qrow = qrow0 + 32 * jq;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1030,7 +1062,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_bwd_dq_ds_kernel(const KParams p
         f32x4* dst = reinterpret_cast<f32x4*>(p.U + qrow * D + 32 * db + 8 * j + 4 * hh);
         f32x4 u = *dst;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] += dq[db][4 * j + i];
+        for (int i = 0; i < 4; ++i) u[i] += dq[jq][db][4 * j + i];
         *dst = u;
       }
   }
@@ -1058,7 +1090,10 @@ int launch_bwd_ds(const KParams& kv, const KParams& q, void* stream, const BwdFo
     if ((e = (int)hipStreamWaitEvent((hipStream_t)fork->side, (hipEvent_t)fork->fork, 0))) return e;
     qs = (hipStream_t)fork->side;
   }
-  hipLaunchKernelGGL(chunk_bwd_dq_ds_kernel<D>, dim3((unsigned)nq), dim3(kNT), 0, qs, q);
+  if (q.dq_qblocks == 2)
+    hipLaunchKernelGGL((chunk_bwd_dq_ds_kernel<D, 2>), dim3((unsigned)nq), dim3(kNT), 0, qs, q);
+  else
+    hipLaunchKernelGGL((chunk_bwd_dq_ds_kernel<D, 1>), dim3((unsigned)nq), dim3(kNT), 0, qs, q);
   if ((e = (int)hipGetLastError())) return e;
   if (qs != (hipStream_t)stream && fork->join) {
     if ((e = (int)hipEventRecord((hipEvent_t)fork->join, qs))) return e;

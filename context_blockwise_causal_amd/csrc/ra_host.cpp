@@ -183,7 +183,14 @@ int run_bwd_ds(const Shape& s, KParams& kp, const ra_pair* pairs, int32_t n, voi
   KParams kq = kp;
   build_ranges(&kp, pairs, n, false, s.D == 128 ? kBwdPPTileRows : kBwdTileRows);
   kp.q_per_wg = kv_heads_per_wg(kp);
-  build_ranges(&kq, pairs, n, true, kBwdDsTileRows);
+  // dQ kernel: two query blocks per wavefront (each K^T operand read from LDS feeds two MFMAs)
+  // while the wider tiles still give a grid of several workgroups per CU; else one
+  build_ranges(&kq, pairs, n, true, 2 * kBwdDsTileRows);
+  kq.dq_qblocks = 2;
+  if ((int64_t)kq.B * kq.Hq * kq.tiles_per_head < kBwdDsWideMin) {
+    build_ranges(&kq, pairs, n, true, kBwdDsTileRows);
+    kq.dq_qblocks = 1;
+  }
   ds_layout(s, pairs, n, &kp);
   ds_layout(s, pairs, n, &kq);
   kp.ds = ds;

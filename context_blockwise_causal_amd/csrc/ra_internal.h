@@ -99,6 +99,7 @@ struct KParams {
   int64_t attn_chunk;     // attention chunk (0 = none)
   int32_t fresh;          // forward: start every row from the empty state instead of loading U, m, l
   int32_t q_per_wg;       // dK/dV kernel (D = 128): query heads of one key/value group per workgroup (0 or 1: one)
+  int32_t dq_qblocks;     // dQ-from-stored-dS kernel: 32-query blocks per wavefront (2, or 0 / 1: one)
   int32_t nranges;
   int64_t tiles_per_head;
   KRange ranges[4];
@@ -179,6 +180,8 @@ constexpr int64_t kBwdTileRows = 128;   // K/V rows per dK/dV workgroup (bf16 MF
 constexpr int64_t kBwdPPTileRows = 256; // K/V rows per dK/dV workgroup of the ping-pong kernel (D = 128)
 constexpr int64_t kBwdQTileRows = 128;  // Q rows per dQ workgroup (bf16 MFMA kernel)
 constexpr int64_t kBwdDsTileRows = 128; // Q rows per workgroup of the dQ-from-stored-dS kernel
+                                         // with one query block per wavefront (twice with two)
+constexpr int64_t kBwdDsWideMin = 512;   // workgroups the two-block dQ grid needs to be chosen
 constexpr int64_t kF32FwdTileRows = 1;  // one row per workgroup in the fp32 path
 constexpr int64_t kF32BwdTileRows = 1;
 

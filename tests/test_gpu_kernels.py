@@ -318,6 +318,41 @@ def test_chunk_bwd_two_query_heads_per_workgroup(ctx, kind, Hkv):
             assert_close(to_f64(got), ref, dtype, f"{name} ({entry})")
 
 
+@pytest.mark.parametrize("kind,window,D", [("FULL", 0, 128), ("DIAG", 0, 128), ("DIAG", 150, 128),
+                                           ("FULL", 0, 64), ("DIAG", 0, 64)])
+def test_chunk_bwd_dq_two_query_blocks_per_wavefront(ctx, kind, window, D):
+    """With at least 1024 dQ workgroups at 256 query rows each, the dQ kernel of the stored-dS
+    entry takes two 32-query blocks per wavefront (tiles of 32 keys x 256 queries, each K^T operand
+    feeding two MFMAs): 2 x 256 query heads over 500 query rows (two tiles per head, the second
+    ragged), a FULL pair with 300 keys and a DIAG pair, also with a sliding window, every element
+    of dQ, dK and dV against the oracle."""
+    B, Hq, dtype = 2, 256, "bf16"
+    Hkv = Hq // 2 if D == 128 else Hq
+    qlen = 500
+    kvlen = 300 if kind == "FULL" else qlen
+    mask = {"FULL": L.RA_MASK_FULL, "DIAG": L.RA_MASK_DIAG}[kind]
+    prob = api.Problem(B, 2 * qlen, Hq, Hkv, D, 1, "contiguous", dtype, 0.0, window, 0)
+    q = to_dev(rand_store((B, Hq, qlen, D), dtype, 131), dtype)
+    k = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 132), dtype)
+    v = to_dev(rand_store((B, Hkv, kvlen, D), dtype, 133), dtype)
+    do = to_dev(rand_store((B, Hq, qlen, D), dtype, 134), dtype)
+    qp, kp = O.pair_positions(O.FULL if kind == "FULL" else O.DIAG, qlen, kvlen)
+    q64, k64, v64, do64 = (to_f64(t) for t in (q, k, v, do))
+    o, lse = O.attention_rows(q64, k64, v64, qp, kp, window=window)
+    delta = np.sum(do64 * o, axis=-1)
+    lse_d = torch.tensor(lse, dtype=torch.float32, device="cuda")
+    dl_d = torch.tensor(delta, dtype=torch.float32, device="cuda")
+    rdq, rdk, rdv = O.attention_rows_bwd(q64, k64, v64, do64, qp, kp, window=window)
+    dq = torch.zeros(B, Hq, qlen, D, device="cuda")
+    dk = torch.zeros(B, Hkv, kvlen, D, device="cuda")
+    dv = torch.zeros_like(dk)
+    chunk_bwd("stored", ctx, prob, q, do, lse_d, dl_d, k, v,
+              [(0, 0, qlen, kvlen, mask, int(qp[0]), int(kp[0]))], dq, dk, dv)
+    torch.cuda.synchronize()
+    for got, ref, name in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
+        assert_close(to_f64(got), ref, dtype, name)
+
+
 @pytest.mark.parametrize("kind", ["FULL", "DIAG"])
 @pytest.mark.parametrize("n", [1, 2, 3])
 def test_short_loops_of_the_d128_kernels(ctx, n, kind):
